@@ -1,0 +1,107 @@
+"""Oracle: the activation-memory ledger of one transformer layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module.
+
+Bytes of stored activations per layer for sequence length s, micro-batch b,
+hidden size h, a attention heads and tensor-parallel size t (2-byte
+activations):
+
+* no recomputation:          sbh (34 + 5 a s / h)   -- per token "34 d + 5 H T"
+  ("Recomputing Activations" plate, "What you will learn")
+* selective recomputation:   34 sbh                  (attention scores re-done)
+* full recomputation:        2 sbh                   (each layer's input only)
+* tensor parallel only:      sbh (10 + 24/t + 5 a s / (h t)); the layer norms and
+  the post-attention / post-MLP dropouts, 10sbh, are replicated on every rank
+  (LIT-736 record, Key takeaways bullet 1)
+* tensor + sequence parallel: the unparallelised figure divided by t
+  (LIT-736 record, Key takeaways bullet 2)
+
+The split of 34 into 10 replicated + 24 divided by t, and of the attention
+term into three a*s^2*b tensors (softmax output 2, dropout mask 1, dropout
+output 2 bytes per element), are the reading that makes the pages' totals
+consistent; the pages print only the totals.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+REPLICATED_PER_SBH = 10        # LN inputs (4) + post-attn/MLP dropout masks (2) + QKV/fc1 inputs (4)
+SPLIT_PER_SBH = 24             # the rest of the 34
+ATTN_SCORE_PER_AS2B = 5        # softmax out (2) + dropout mask (1) + dropout out (2)
+
+
+@dataclass(frozen=True)
+class LayerDims:
+    s: int
+    b: int
+    h: int
+    a: int
+
+
+def bytes_none(d: LayerDims) -> float:
+    return d.s * d.b * d.h * (34 + 5 * d.a * d.s / d.h)
+
+
+def bytes_selective(d: LayerDims) -> float:
+    return 34.0 * d.s * d.b * d.h
+
+
+def bytes_full(d: LayerDims) -> float:
+    return 2.0 * d.s * d.b * d.h
+
+
+def bytes_tp(d: LayerDims, t: int, selective: bool = False) -> float:
+    """Tensor parallel without sequence parallel: the 10sbh term stays whole."""
+    sbh = d.s * d.b * d.h
+    attn = 0.0 if selective else ATTN_SCORE_PER_AS2B * d.a * d.s * d.s * d.b / t
+    return REPLICATED_PER_SBH * sbh + SPLIT_PER_SBH * sbh / t + attn
+
+
+def bytes_tp_sp(d: LayerDims, t: int, selective: bool = False) -> float:
+    """Tensor + sequence parallel: every term divides by t."""
+    return (bytes_selective(d) if selective else bytes_none(d)) / t
+
+
+def per_token_bytes(d_model: int, heads: int, seq: int, mode: str) -> float:
+    """The per-token, per-layer form: 34 d + 5 H T / 34 d / 2 d."""
+    if mode == "none":
+        return 34 * d_model + 5 * heads * seq
+    if mode == "selective":
+        return 34 * d_model
+    if mode == "full":
+        return 2 * d_model
+    raise ValueError(mode)
+
+
+def model_bytes(d: LayerDims, layers: int, mode: str) -> float:
+    f = {"none": bytes_none, "selective": bytes_selective, "full": bytes_full}[mode]
+    return layers * f(d)
+
+
+def full_recompute_flops_ratio() -> float:
+    """Training goes from about 6N to 8N FLOPs per token with a second forward."""
+    return 8.0 / 6.0
+
+
+def selective_recompute_extra(n_params: float, d: LayerDims, layers: int,
+                              causal: bool = True) -> float:
+    """Extra compute of re-doing the score FLOPs (QK^T and PV forward).
+
+    Reading of the plate's "selective figure is the attention-score FLOPs
+    re-done": forward score FLOPs per token per layer are 4 s h (2 s h causal);
+    the base is 6N plus the attention FLOPs of forward + backward (3x forward).
+    """
+    fwd = (2.0 if causal else 4.0) * d.s * d.h * layers
+    return fwd / (6.0 * n_params + 3.0 * fwd)
+
+
+def kept_bytes_this_library(s, b, hq, d_head, dtype_bytes=2, norm="layernorm"):
+    """Bytes the attention core and the norm region of this library keep.
+
+    Attention core: Q, K, V, O (dtype) + LSE (fp32 per query row and head).
+    Norm region: h (dtype) + mean/rstd (fp32 per row).  No s^2 term.
+    """
+    qkvo = 4 * b * s * hq * d_head * dtype_bytes
+    lse = 4 * b * hq * s
+    stats = (8 if norm == "layernorm" else 4) * s * b
+    return qkvo + lse + stats
