@@ -1,0 +1,101 @@
+// Launch parameters and launchers shared between the kernels and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace srat {
+
+// ---------------------------------------------------------------- norm region
+struct NormFwdParams {
+  const void* resid;
+  const void* y;
+  const float* gamma;
+  const float* beta;
+  void* h;
+  void* u;
+  float* mean;
+  float* rstd;
+  int64_t rows;
+  int32_t b;
+  int32_t hdim;
+  int64_t seq_offset;
+  float eps;
+  float inv_keep;      // 1 / (1 - p)
+  uint32_t thresh;     // 16-bit drop threshold, 0 = no dropout
+  uint32_t k0, k1;     // Philox key
+  uint32_t tag;        // word 3 of the hidden-dropout counter
+};
+
+struct NormBwdParams {
+  const void* du;
+  const void* dres;
+  const void* h;
+  const float* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dh;
+  void* dy;            // == dh allowed when thresh == 0
+  float* partial;      // [blocks][2][hdim] dgamma / dbeta partial sums
+  float* dgamma;
+  float* dbeta;
+  int64_t rows;
+  int32_t rows_per_block;
+  int32_t b;
+  int32_t hdim;
+  int64_t seq_offset;
+  float inv_keep;
+  uint32_t thresh, k0, k1, tag;
+};
+
+// Returns the number of blocks the backward row kernel will use (for the workspace).
+int norm_bwd_blocks(int64_t rows, int hdim);
+hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStream_t st);
+hipError_t launch_norm_bwd(const NormBwdParams& p, bool bf16, bool rms, hipStream_t st);
+hipError_t launch_hidden_mask(const NormFwdParams& p, uint8_t* mask, hipStream_t st);
+
+// ------------------------------------------------------------ attention core
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;       // forward output (read by the backward)
+  const float* lse;
+  const void* dout;
+  void* out;           // forward: O
+  float* lse_out;      // forward: LSE
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;       // [b, s, hq, d] fp32 workspace
+  float* dk_part;      // grouped-query attention: [b, s, hq, d] fp32 per-q-head partials
+  float* dv_part;
+  float* delta;        // [b, hq, s] rowsum(dO * O)
+  int64_t sq_b, sq_s, sq_h;
+  int64_t sk_b, sk_s, sk_h;
+  int64_t sv_b, sv_s, sv_h;
+  int64_t so_b, so_s, so_h;
+  int32_t b, s, hq, hkv, d;
+  int32_t causal;
+  float scale;
+  float scale_log2;    // scale * log2(e)
+  float inv_keep;      // 1 / (1 - p)
+  uint32_t thresh;     // 16-bit drop threshold, 0 = no dropout
+  uint32_t k0, k1;
+  int32_t head_offset;
+};
+
+hipError_t launch_attn_fwd(const AttnParams& p, bool bf16, hipStream_t st);
+hipError_t launch_attn_bwd(const AttnParams& p, bool bf16, hipStream_t st);
+hipError_t launch_attn_mask(const AttnParams& p, uint8_t* mask, hipStream_t st);
+
+// tracing: records a start event before and a stop event after a launch
+struct TraceScope {
+  TraceScope(const char* name, hipStream_t st);
+  ~TraceScope();
+  const char* name_;
+  hipStream_t st_;
+  void* ev_[2];
+};
+
+}  // namespace srat

@@ -1,0 +1,241 @@
+"""Python binding of libsrat (ctypes): argument marshalling only.
+
+Every step of the attention core and of the norm region runs in the HIP
+library; this module builds descriptors, allocates outputs and workspaces
+with torch on the tensors' device, and passes raw pointers plus torch's
+current HIP stream.  If libsrat.so is missing, every call raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsrat.so")
+
+SRAT_F32, SRAT_BF16 = 1, 2
+SRAT_LAYERNORM, SRAT_RMSNORM = 1, 2
+ERRORS = {-1: "SRAT_ERR_INVALID", -2: "SRAT_ERR_UNSUPPORTED", -3: "SRAT_ERR_WORKSPACE", -4: "SRAT_ERR_HIP"}
+EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_bwd", "srat_attn_core_bwd_workspace", "srat_sp_norm_fwd",
+           "srat_sp_norm_bwd", "srat_sp_norm_bwd_workspace", "srat_dropout_mask_dump", "srat_trace_enable",
+           "srat_trace_read", "srat_last_error", "srat_version")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("b", ctypes.c_int64), ("s", ctypes.c_int64), ("hq", ctypes.c_int64),
+                ("hkv", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+                ("scale", ctypes.c_float), ("p_drop", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("head_offset", ctypes.c_int64)]
+
+
+class NormDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
+                ("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("seq_offset", ctypes.c_int64), ("eps", ctypes.c_float), ("p_drop", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("site", ctypes.c_int32)]
+
+
+class TraceEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+class SratError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open libsrat.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SratError(f"{LIB_PATH} not found: build it with "
+                            "`python -m selective_recompute_attention_attn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.srat_attn_core_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp]
+        L.srat_attn_core_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.srat_attn_core_bwd_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
+        L.srat_sp_norm_fwd.argtypes = [ctypes.POINTER(NormDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.srat_sp_norm_bwd.argtypes = [ctypes.POINTER(NormDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.srat_sp_norm_bwd_workspace.argtypes = [ctypes.POINTER(NormDesc), ctypes.POINTER(sz)]
+        L.srat_dropout_mask_dump.argtypes = [ctypes.c_int, vp, vp, vp]
+        L.srat_trace_enable.argtypes = [ctypes.c_int]
+        L.srat_trace_read.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int, ctypes.c_int]
+        L.srat_last_error.restype = ctypes.c_char_p
+        for f in EXPORTS:
+            if f != "srat_last_error":
+                getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().srat_last_error().decode()
+        raise SratError(f"{what}: {ERRORS.get(rc, rc)}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SRAT_BF16
+    if t.dtype == torch.float32:
+        return SRAT_F32
+    raise SratError(f"unsupported dtype {t.dtype}")
+
+
+def _strides(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise SratError("attention tensors are [b, s, heads, d] with d contiguous")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def attn_desc(q, k, v, o, *, causal: bool, scale: Optional[float], p_drop: float, seed: int,
+              head_offset: int) -> AttnDesc:
+    b, s, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, s, hkv, d) or v.shape != k.shape or o.shape != q.shape:
+        raise SratError("shape mismatch between q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise SratError("q, k, v, o must share a dtype")
+    return AttnDesc(dtype=_dtype_code(q), causal=int(bool(causal)), b=b, s=s, hq=hq, hkv=hkv, d=d,
+                    q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o),
+                    scale=float(1.0 / math.sqrt(d) if scale is None else scale), p_drop=float(p_drop),
+                    seed=int(seed) & 0xFFFFFFFFFFFFFFFF, head_offset=int(head_offset))
+
+
+def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                  scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = dropout(softmax(q k^T * scale)) v and the per-row LSE [b, hq, s] (fp32)."""
+    b, s, hq, d = q.shape
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    l = torch.empty((b, hq, s), dtype=torch.float32, device=q.device) if lse is None else lse
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    _check(lib().srat_attn_core_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+                                    _stream(q.device)), "srat_attn_core_fwd")
+    return o, l
+
+
+def attn_bwd_workspace_bytes(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().srat_attn_core_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "srat_attn_core_bwd_workspace")
+    return n.value
+
+
+def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
+                  p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
+                  workspace: Optional[torch.Tensor] = None):
+    """dq, dk, dv by recomputation of scores, softmax and dropout mask."""
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise SratError("dout must have o's shape and strides")
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    need = attn_bwd_workspace_bytes(desc)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().srat_attn_core_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                    _stream(q.device)), "srat_attn_core_bwd")
+    return dq, dk, dv
+
+
+def norm_desc(x: torch.Tensor, *, norm: str, eps: float, p_drop: float, seed: int, site: int,
+              seq_offset: int) -> NormDesc:
+    if x.dim() != 3 or not x.is_contiguous():
+        raise SratError("norm-region tensors are contiguous [s_local, b, h]")
+    kind = {"layernorm": SRAT_LAYERNORM, "rmsnorm": SRAT_RMSNORM}[norm]
+    s_local, b, h = x.shape
+    return NormDesc(dtype=_dtype_code(x), norm=kind, s_local=s_local, b=b, h=h, seq_offset=int(seq_offset),
+                    eps=float(eps), p_drop=float(p_drop), seed=int(seed) & 0xFFFFFFFFFFFFFFFF, site=int(site))
+
+
+def sp_norm_fwd(resid, y, gamma, beta=None, *, norm: str = "layernorm", eps: float = 1e-5,
+                p_drop: float = 0.0, seed: int = 0, site: int = 1, seq_offset: int = 0):
+    """h = resid + dropout(y); u = norm(h) * gamma (+ beta).  Returns h, u, mean, rstd."""
+    if y.shape != resid.shape or y.dtype != resid.dtype:
+        raise SratError("resid and y must match")
+    desc = norm_desc(resid, norm=norm, eps=eps, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    rows = resid.shape[0] * resid.shape[1]
+    h = torch.empty_like(resid)
+    u = torch.empty_like(resid)
+    mean = torch.empty(rows, dtype=torch.float32, device=resid.device) if norm == "layernorm" else None
+    rstd = torch.empty(rows, dtype=torch.float32, device=resid.device)
+    _check(lib().srat_sp_norm_fwd(ctypes.byref(desc), _ptr(resid), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(h),
+                                  _ptr(u), _ptr(mean), _ptr(rstd), _stream(resid.device)), "srat_sp_norm_fwd")
+    return h, u, mean, rstd
+
+
+def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_drop: float = 0.0,
+                seed: int = 0, site: int = 1, seq_offset: int = 0, alias_dy: bool = False,
+                workspace: Optional[torch.Tensor] = None):
+    """dh (= d resid), dy, dgamma, dbeta (None for RMSNorm)."""
+    desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    dh = torch.empty_like(h)
+    dy = dh if alias_dy else torch.empty_like(h)
+    hdim = h.shape[2]
+    dgamma = torch.empty(hdim, dtype=torch.float32, device=h.device)
+    dbeta = torch.empty(hdim, dtype=torch.float32, device=h.device) if norm == "layernorm" else None
+    n = ctypes.c_size_t(0)
+    _check(lib().srat_sp_norm_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)), "srat_sp_norm_bwd_workspace")
+    ws = workspace if workspace is not None else torch.empty(max(n.value, 1), dtype=torch.uint8, device=h.device)
+    _check(lib().srat_sp_norm_bwd(ctypes.byref(desc), _ptr(du), _ptr(dres), _ptr(h), _ptr(gamma), _ptr(mean),
+                                  _ptr(rstd), _ptr(dh), _ptr(dy), _ptr(dgamma), _ptr(dbeta), _ptr(ws),
+                                  ws.numel(), _stream(h.device)), "srat_sp_norm_bwd")
+    return dh, dy, dgamma, dbeta
+
+
+def attn_dropout_mask(b, s, hq, *, p_drop, seed, head_offset=0, device="cuda"):
+    """The attention keep mask [b, hq, s, s] (uint8) the kernels use (small shapes only)."""
+    d = 32
+    z = torch.empty((b, s, hq, d), dtype=torch.bfloat16, device=device)
+    desc = attn_desc(z, z, z, z, causal=False, scale=1.0, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    m = torch.empty((b, hq, s, s), dtype=torch.uint8, device=device)
+    _check(lib().srat_dropout_mask_dump(0, ctypes.cast(ctypes.pointer(desc), ctypes.c_void_p), _ptr(m),
+                                        _stream(m.device)), "srat_dropout_mask_dump")
+    return m
+
+
+def hidden_dropout_mask(s_local, b, h, *, p_drop, seed, site=1, seq_offset=0, device="cuda"):
+    """The hidden-dropout keep mask [s_local, b, h] (uint8) the kernels use."""
+    z = torch.empty((s_local, b, h), dtype=torch.bfloat16, device=device)
+    desc = norm_desc(z, norm="layernorm", eps=1e-5, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    m = torch.empty((s_local, b, h), dtype=torch.uint8, device=device)
+    _check(lib().srat_dropout_mask_dump(1, ctypes.cast(ctypes.pointer(desc), ctypes.c_void_p), _ptr(m),
+                                        _stream(m.device)), "srat_dropout_mask_dump")
+    return m
+
+
+def trace_enable(on: bool = True) -> None:
+    _check(lib().srat_trace_enable(int(on)), "srat_trace_enable")
+
+
+def trace_read(reset: bool = True):
+    """{kernel name: (launches, total_ms)} accumulated since the last reset."""
+    cap = 64
+    buf = (TraceEntry * cap)()
+    n = lib().srat_trace_read(buf, cap, int(reset))
+    if n < 0:
+        _check(n, "srat_trace_read")
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, cap))}

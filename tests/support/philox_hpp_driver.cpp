@@ -1,0 +1,16 @@
+// Host build of the library's own philox.hpp (the code the kernels use), for
+// a bit-exact check against the oracle.  Reads "seed c0 c1 c2 c3 thresh" lines,
+// prints the four words and the eight keep bits.
+#include <cstdio>
+#include "philox.hpp"
+
+int main() {
+  unsigned long long seed, c0, c1, c2, c3, t;
+  while (std::scanf("%llu %llu %llu %llu %llu %llu", &seed, &c0, &c1, &c2, &c3, &t) == 6) {
+    const srat::Philox4 r = srat::philox4x32_10((uint32_t)c0, (uint32_t)c1, (uint32_t)c2, (uint32_t)c3,
+                                                (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32));
+    std::printf("%08x %08x %08x %08x %02x\n", r.w[0], r.w[1], r.w[2], r.w[3],
+                srat::keep_bits8(r, (uint32_t)t));
+  }
+  return 0;
+}

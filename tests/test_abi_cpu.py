@@ -1,0 +1,168 @@
+"""The C-ABI library on the CPU: it loads, exports what include/srat.h declares,
+validates arguments before any HIP call, and its Philox agrees with the oracle."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from oracle import philox as ph
+from selective_recompute_attention_attn_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "srat.h")
+CSRC = os.path.join(ROOT, "selective_recompute_attention_attn_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libsrat.so is not built (run __graft_entry__.build())")
+    return ops.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(srat_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ops.EXPORTS)
+    assert L.srat_version() == 1
+
+
+def _desc(**kw):
+    base = dict(dtype=ops.SRAT_BF16, causal=1, b=1, s=256, hq=4, hkv=4, d=64,
+                q_stride=(256 * 4 * 64, 4 * 64, 64), k_stride=(256 * 4 * 64, 4 * 64, 64),
+                v_stride=(256 * 4 * 64, 4 * 64, 64), o_stride=(256 * 4 * 64, 4 * 64, 64),
+                scale=0.125, p_drop=0.1, seed=0, head_offset=0)
+    base.update(kw)
+    for k in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        base[k] = (ctypes.c_int64 * 3)(*base[k])
+    return ops.AttnDesc(**base)
+
+
+def _err(L, rc):
+    return rc, L.srat_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=48), -2), (dict(d=256), -2), (dict(p_drop=1.0), -1), (dict(p_drop=-0.1), -1),
+    (dict(hq=4, hkv=3), -1), (dict(dtype=7), -1), (dict(causal=2), -1), (dict(s=-1), -1),
+    (dict(q_stride=(256 * 4 * 64, 4 * 64, 60)), -1), (dict(k_stride=(0, 3, 64)), -1),
+    (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1)])
+def test_attention_validation_before_any_hip_call(L, kw, code):
+    d = _desc(**kw)
+    n = ctypes.c_size_t(0)
+    rc, msg = _err(L, L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)))
+    assert rc == code and msg
+    # forward with NULL tensors: the descriptor error comes first
+    rc, msg = _err(L, L.srat_attn_core_fwd(ctypes.byref(d), None, None, None, None, None, None))
+    assert rc == code and msg
+
+
+def test_null_descriptor_and_null_pointers(L):
+    assert L.srat_attn_core_fwd(None, None, None, None, None, None, None) == -1
+    d = _desc()
+    rc, msg = _err(L, L.srat_attn_core_fwd(ctypes.byref(d), None, None, None, None, None, None))
+    assert rc == -1 and "NULL" in msg
+    odd = ctypes.c_void_p(0x1002)
+    rc, msg = _err(L, L.srat_attn_core_fwd(ctypes.byref(d), odd, odd, odd, odd, odd, None))
+    assert rc == -1
+    rc, msg = _err(L, L.srat_attn_core_bwd(ctypes.byref(d), *([ctypes.c_void_p(0x1000)] * 9),
+                                           ctypes.c_void_p(0x1000), 16, None))
+    assert rc == -3 and "workspace" in msg
+
+
+def test_workspace_is_linear_in_s_never_quadratic(L):
+    sizes = []
+    for s in (1024, 2048, 4096, 8192):
+        qs, ks = (s * 8 * 128, 8 * 128, 128), (s * 128, 128, 128)
+        d = _desc(s=s, hq=8, hkv=1, d=128, q_stride=qs, o_stride=qs, k_stride=ks, v_stride=ks)
+        n = ctypes.c_size_t(0)
+        assert L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+        sizes.append(n.value)
+        assert n.value < 2 * 8 * s * s      # below one bf16 s x s matrix per q-head
+    for a, b in zip(sizes, sizes[1:]):
+        assert b == pytest.approx(2 * a, rel=1e-3)
+
+
+def _ndesc(**kw):
+    base = dict(dtype=ops.SRAT_BF16, norm=ops.SRAT_LAYERNORM, s_local=256, b=4, h=6144, seq_offset=0,
+                eps=1e-5, p_drop=0.1, seed=0, site=1)
+    base.update(kw)
+    return ops.NormDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=100), -2), (dict(h=65536), -2), (dict(norm=3), -1), (dict(p_drop=1.0), -1),
+    (dict(site=200), -1), (dict(b=0), -1), (dict(eps=-1.0), -1), (dict(seq_offset=-5), -1)])
+def test_norm_validation_before_any_hip_call(L, kw, code):
+    d = _ndesc(**kw)
+    n = ctypes.c_size_t(0)
+    rc, msg = _err(L, L.srat_sp_norm_bwd_workspace(ctypes.byref(d), ctypes.byref(n)))
+    assert rc == code and msg
+
+
+def test_norm_alias_rule_and_workspace(L):
+    d = _ndesc()
+    n = ctypes.c_size_t(0)
+    assert L.srat_sp_norm_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert 0 < n.value <= 256 * 2 * 6144 * 4 + 256
+    p = ctypes.c_void_p(0x10000)
+    rc, msg = _err(L, L.srat_sp_norm_bwd(ctypes.byref(d), p, p, p, p, p, p, p, p, p, p, p, n.value, None))
+    assert rc == -1 and "alias" in msg
+
+
+def test_trace_read_empty(L):
+    assert L.srat_trace_enable(0) == 0
+    assert L.srat_trace_read(None, 0, 1) >= 0
+
+
+@pytest.fixture(scope="module")
+def philox_hpp():
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no g++")
+    out = os.path.join(tempfile.mkdtemp(prefix="srat_hpp_"), "drv")
+    subprocess.run([cxx, "-O2", f"-I{CSRC}", os.path.join(ROOT, "tests", "support", "philox_hpp_driver.cpp"),
+                    "-o", out], check=True, capture_output=True)
+    return out
+
+
+def test_library_philox_equals_oracle(philox_hpp):
+    rng = np.random.default_rng(3)
+    rows = []
+    for _ in range(2000):
+        seed = int(rng.integers(0, 2**63)) * 2 + 1
+        c = [int(x) for x in rng.integers(0, 2**32, size=4, dtype=np.uint64)]
+        t = int(rng.choice([0, 1, 6554, 32768, 65535]))
+        rows.append((seed, *c, t))
+    inp = "".join(" ".join(map(str, r)) + "\n" for r in rows)
+    res = subprocess.run([philox_hpp], input=inp, capture_output=True, text=True, check=True)
+    for r, ln in zip(rows, res.stdout.strip().splitlines()):
+        seed, c0, c1, c2, c3, t = r
+        words = ph.philox4x32_10(c0, c1, c2, c3, seed & 0xFFFFFFFF, seed >> 32)
+        parts = ln.split()
+        assert [int(x, 16) for x in parts[:4]] == [int(w) for w in words]
+        bits = 0
+        for e in range(8):
+            u = (int(words[e >> 1]) >> (16 * (e & 1))) & 0xFFFF
+            bits |= int(u >= t) << e
+        assert int(parts[4], 16) == bits
+
+
+def test_threshold_rule_matches_oracle():
+    # the host code computes T from the float probability in double precision
+    for p in (0.0, 0.1, 0.25, 0.3333, 0.9999):
+        t = int(float(np.float32(p)) * 65536.0 + 0.5)
+        assert t == ph.drop_threshold(p)
