@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+One step = attention-core forward + backward (recompute) + sequence-parallel
+norm-region forward + backward, on one tensor-parallel rank's share of a
+workload (default: the 22B GPT layer at t = 8), with seeded synthetic inputs
+already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+value       attention-core fwd+bwd algorithmic TFLOP/s, timed with HIP events
+            around the attention calls of each timed step
+roofline    the dominant kernel (largest share of the traced time): its
+            algorithmic work per launch / its mean launch time (library trace
+            events on the launch stream), against MI355X's published peak
+cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn-core fwd+bwd TFLOP/s & % bf16 MFMA peak; SP LayerNorm GB/s (1 GPU)"
+PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+PEAK_HBM_GBPS = 8000.0
+N_SETS = 4                      # rotated input/output sets (> 2x the 256 MB last-level cache)
+
+
+def attn_flops(a, fwd=True, bwd=True):
+    """Algorithmic FLOPs: 4 (QK^T, PV) forward + 10 (QK^T recompute, dP, dV, dK, dQ)
+    backward per score element and head-dim unit; causal counts half the scores."""
+    units = a.b * a.hq * a.s * a.s * a.d * (0.5 if a.causal else 1.0)
+    return units * ((4 if fwd else 0) + (10 if bwd else 0))
+
+
+def norm_bytes(n, fwd=True):
+    """Algorithmic HBM bytes: fwd reads resid, y and writes h, u; bwd reads du, dres, h
+    and writes dh, dy (dy is dh when p = 0); plus per-row statistics and [h] vectors."""
+    e = 2 if n.dtype == "bf16" else 4
+    elems = n.rows * n.h
+    stats = n.rows * (8 if n.norm == "layernorm" else 4)
+    vecs = n.h * 4 * (2 if n.norm == "layernorm" else 1)
+    if fwd:
+        return elems * 4 * e + stats + vecs
+    tensors = 5 if n.p_drop > 0 else 4
+    return elems * tensors * e + stats + 2 * vecs
+
+
+def src_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "attn_bwd_bf16": ["selective_recompute_attention_attn_amd/csrc/attn_bwd.hip",
+                      "selective_recompute_attention_attn_amd/csrc/philox.hpp",
+                      "selective_recompute_attention_attn_amd/csrc/common.hpp"],
+    "attn_fwd_bf16": ["selective_recompute_attention_attn_amd/csrc/attn_fwd.hip",
+                      "selective_recompute_attention_attn_amd/csrc/philox.hpp",
+                      "selective_recompute_attention_attn_amd/csrc/common.hpp"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash(*KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds_budget=20.0):
+    """Time the float64 oracle on a bounded sample: a few (batch, head) pairs of
+    the attention core (fwd + recompute bwd) and some rows of the norm region."""
+    import numpy as np
+    from oracle import attention as oat
+    from oracle import norm as onm
+    from selective_recompute_attention_attn_amd import gen
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    a, n = w.attn, w.norm
+    x = gen.attn_inputs(a)
+    kw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed)
+    heads, t_attn = [], 0.0
+    grp = a.hq // a.hkv
+    for bb in range(a.b):
+        for hh in range(0, a.hq, grp):
+            t0 = time.perf_counter()
+            o, lse = oat.attn_fwd(x["q"], x["k"], x["v"], heads=[(bb, hh)], **kw)
+            oat.attn_bwd(x["q"], x["k"], x["v"], lse, x["do"], heads=[(bb, hh)], **kw)
+            t_attn += time.perf_counter() - t0
+            heads.append((bb, hh))
+            if t_attn > seconds_budget * 0.8 or len(heads) >= 8:
+                break
+        if t_attn > seconds_budget * 0.8 or len(heads) >= 8:
+            break
+    per_head = attn_flops(a) / (a.b * a.hq)
+    tflops = per_head * len(heads) / t_attn / 1e12
+    y = gen.norm_inputs(n)
+    rows = max(1, min(n.s_local, 64))
+    nkw = dict(norm=n.norm, p_drop=n.p_drop, seed=n.seed, site=n.site)
+    t0 = time.perf_counter()
+    h, u, mu, rs = onm.sp_norm_fwd(y["resid"][:rows], y["y"][:rows], y["gamma"], y["beta"], eps=n.eps, **nkw)
+    onm.sp_norm_bwd(y["du"][:rows], y["dres"][:rows], h, y["gamma"], mu, rs, **nkw)
+    t_norm = time.perf_counter() - t0
+    sub = n.with_(s_local=rows)
+    gbps = (norm_bytes(sub, True) + norm_bytes(sub, False)) / t_norm / 1e9
+    return {"value": tflops, "unit": "TFLOP/s", "cores": blas_threads or len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {a.b * a.hq} (batch, q-head) pairs: attention fwd + recompute bwd in "
+                      f"float64 numpy with the full {a.s}x{a.s} score matrix ({t_attn:.1f} s; BLAS threads "
+                      f"{blas_threads}, elementwise single-threaded); norm region {rows * n.b} of {n.rows} rows "
+                      f"fwd+bwd at {gbps:.3f} GB/s",
+            "norm_gbps": gbps, "host_cores": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt22b-t8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="time without per-launch trace events")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_recompute_attention_attn_amd import gen, ops
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ops.lib()
+    dev = torch.device("cuda:0")
+    w = gen.WORKLOADS[args.workload]
+    a, n = w.attn, w.norm
+    tdt = torch.bfloat16 if a.dtype == "bf16" else torch.float32
+    ndt = torch.bfloat16 if n.dtype == "bf16" else torch.float32
+
+    def t(x, dt):
+        return torch.from_numpy(x).to(dt).to(dev)
+
+    xa = gen.attn_inputs(a)
+    xn = gen.norm_inputs(n)
+    sets = []
+    for _ in range(N_SETS):
+        s = {k: t(xa[k], tdt) for k in ("q", "k", "v", "do")}
+        s["o"] = torch.empty_like(s["q"])
+        s["lse"] = torch.empty((a.b, a.hq, a.s), dtype=torch.float32, device=dev)
+        s["grads"] = (torch.empty_like(s["q"]), torch.empty_like(s["k"]), torch.empty_like(s["v"]))
+        for k in ("resid", "y", "du", "dres"):
+            s[k] = t(xn[k], ndt)
+        s["gamma"] = torch.tensor(xn["gamma"], device=dev)
+        s["beta"] = torch.tensor(xn["beta"], device=dev)
+        ln = n.norm == "layernorm"
+        s["nf"] = (torch.empty_like(s["resid"]), torch.empty_like(s["resid"]),
+                   torch.empty(n.rows, dtype=torch.float32, device=dev) if ln else None,
+                   torch.empty(n.rows, dtype=torch.float32, device=dev))
+        dh = torch.empty_like(s["resid"])
+        s["nb"] = (dh, dh if n.p_drop == 0 else torch.empty_like(s["resid"]),
+                   torch.empty(n.h, dtype=torch.float32, device=dev),
+                   torch.empty(n.h, dtype=torch.float32, device=dev) if ln else None)
+        sets.append(s)
+    desc = ops.attn_desc(sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["o"], causal=a.causal,
+                         scale=a.scale, p_drop=a.p_drop, seed=a.seed, head_offset=0)
+    ws_attn = torch.empty(ops.attn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    ndesc = ops.norm_desc(sets[0]["resid"], norm=n.norm, eps=n.eps, p_drop=n.p_drop, seed=n.seed, site=n.site,
+                          seq_offset=0)
+    ws_norm = torch.empty(max(ops.sp_norm_bwd_workspace_bytes(ndesc), 1), dtype=torch.uint8, device=dev)
+    akw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed)
+    nkw = dict(norm=n.norm, p_drop=n.p_drop, seed=n.seed, site=n.site)
+
+    def step(i, ev=None):
+        s = sets[i % N_SETS]
+        if ev is not None:
+            ev[0].record()
+        ops.attn_core_fwd(s["q"], s["k"], s["v"], out=s["o"], lse=s["lse"], **akw)
+        ops.attn_core_bwd(s["q"], s["k"], s["v"], s["o"], s["lse"], s["do"], workspace=ws_attn,
+                          outs=s["grads"], **akw)
+        if ev is not None:
+            ev[1].record()
+        h, u, mu, rs = ops.sp_norm_fwd(s["resid"], s["y"], s["gamma"], s["beta"], eps=n.eps, outs=s["nf"], **nkw)
+        if ev is not None:
+            ev[2].record()
+        ops.sp_norm_bwd(s["du"], s["dres"], h, s["gamma"], mu, rs, workspace=ws_norm, outs=s["nb"], **nkw)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    if not args.no_trace:
+        ops.trace_enable(True)
+        ops.trace_read(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    trace = {}
+    if not args.no_trace:
+        trace = ops.trace_read(reset=True)
+        ops.trace_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    nf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    nb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    flops = attn_flops(a)
+    value = flops / (attn_ms * 1e-3) / 1e12
+
+    kernels = {k: {"launches": v[0], "mean_us": 1e3 * v[1] / max(v[0], 1)} for k, v in trace.items()}
+    roofline = None
+    if kernels:
+        dom = max(trace, key=lambda k: trace[k][1])
+        mean_s = trace[dom][1] / trace[dom][0] * 1e-3
+        work = {"attn_bwd_bf16": ("mfma", attn_flops(a, fwd=False, bwd=True)),
+                "attn_fwd_bf16": ("mfma", attn_flops(a, fwd=True, bwd=False)),
+                "sp_norm_fwd": ("hbm", norm_bytes(n, True)),
+                "sp_norm_bwd": ("hbm", norm_bytes(n, False))}
+        if dom in work:
+            bound, amount = work[dom]
+            if bound == "mfma":
+                achieved, peak, unit = amount / mean_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+            else:
+                achieved, peak, unit = amount / mean_s / 1e9, PEAK_HBM_GBPS, "GB/s"
+            roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                        "frac": achieved / peak, "traffic": measured_traffic(dom, w.name),
+                        "mean_launch_us": mean_s * 1e6}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "b": a.b, "s": a.s, "hq": a.hq, "hkv": a.hkv, "d": a.d,
+                   "causal": a.causal, "p_attn": a.p_drop, "norm": n.norm, "norm_rows": n.rows, "h": n.h,
+                   "p_hidden": n.p_drop, "parallelism": "one tensor-parallel rank (t=8) on 1 GPU"},
+        "attn_frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+        "attn_ms": attn_ms,
+        "attn_fwd_tflops": (attn_flops(a, True, False) / (kernels["attn_fwd_bf16"]["mean_us"] * 1e-6) / 1e12
+                            if "attn_fwd_bf16" in kernels else None),
+        "attn_bwd_tflops": (attn_flops(a, False, True) / (kernels["attn_bwd_bf16"]["mean_us"] * 1e-6) / 1e12
+                            if "attn_bwd_bf16" in kernels else None),
+        "sp_fwd_gbps": norm_bytes(n, True) / (nf_ms * 1e-3) / 1e9,
+        "sp_bwd_gbps": norm_bytes(n, False) / (nb_ms * 1e-3) / 1e9,
+        "sp_fwd_frac_of_hbm": norm_bytes(n, True) / (nf_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "sp_bwd_frac_of_hbm": norm_bytes(n, False) / (nb_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

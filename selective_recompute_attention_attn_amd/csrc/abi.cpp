@@ -44,8 +44,17 @@ struct TraceState {
   bool on = false;
   struct Pending { std::string name; hipEvent_t a, b; };
   std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;   // recorded-and-read events, reused
   struct Acc { int64_t n = 0; double ms = 0; };
   std::map<std::string, Acc> acc;
+  bool take(hipEvent_t* e) {
+    if (!pool.empty()) {
+      *e = pool.back();
+      pool.pop_back();
+      return true;
+    }
+    return hipEventCreate(e) == hipSuccess;
+  }
 };
 TraceState& trace() {
   static TraceState t;
@@ -156,8 +165,8 @@ TraceScope::TraceScope(const char* name, hipStream_t st) : name_(name), st_(st) 
   std::lock_guard<std::mutex> lk(t.mu);
   if (!t.on) return;
   hipEvent_t a, b;
-  if (hipEventCreate(&a) != hipSuccess) return;
-  if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+  if (!t.take(&a)) return;
+  if (!t.take(&b)) { t.pool.push_back(a); return; }
   ev_[0] = a;
   ev_[1] = b;
   (void)hipEventRecord(a, st);
@@ -339,8 +348,8 @@ int srat_trace_read(srat_trace_entry* out, int cap, int reset) {
     hipError_t e = hipEventSynchronize(pd.b);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, pd.a, pd.b);
-    (void)hipEventDestroy(pd.a);
-    (void)hipEventDestroy(pd.b);
+    t.pool.push_back(pd.a);
+    t.pool.push_back(pd.b);
     if (e != hipSuccess) {
       t.pending.clear();
       return hip_fail(e, "trace event");

@@ -145,16 +145,26 @@ def attn_bwd_workspace_bytes(desc: AttnDesc) -> int:
 
 def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
                   p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
-                  workspace: Optional[torch.Tensor] = None):
-    """dq, dk, dv by recomputation of scores, softmax and dropout mask."""
+                  workspace: Optional[torch.Tensor] = None, outs=None):
+    """dq, dk, dv by recomputation of scores, softmax and dropout mask.
+
+    outs: optional preallocated (dq, dk, dv) with the strides of (q, k, v).
+    """
     if dout.shape != o.shape or dout.stride() != o.stride():
         raise SratError("dout must have o's shape and strides")
     desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
-    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
-    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
-    need = attn_bwd_workspace_bytes(desc)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if outs is None:
+        dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+        dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    else:
+        dq, dk, dv = outs
+        for t, ref in ((dq, q), (dk, k), (dv, v)):
+            if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+                raise SratError("preallocated gradients must match q, k, v")
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=q.device)
+    ws = workspace
     _check(lib().srat_attn_core_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                                     _stream(q.device)), "srat_attn_core_bwd")
@@ -172,34 +182,52 @@ def norm_desc(x: torch.Tensor, *, norm: str, eps: float, p_drop: float, seed: in
 
 
 def sp_norm_fwd(resid, y, gamma, beta=None, *, norm: str = "layernorm", eps: float = 1e-5,
-                p_drop: float = 0.0, seed: int = 0, site: int = 1, seq_offset: int = 0):
-    """h = resid + dropout(y); u = norm(h) * gamma (+ beta).  Returns h, u, mean, rstd."""
+                p_drop: float = 0.0, seed: int = 0, site: int = 1, seq_offset: int = 0, outs=None):
+    """h = resid + dropout(y); u = norm(h) * gamma (+ beta).  Returns h, u, mean, rstd.
+
+    outs: optional preallocated (h, u, mean, rstd); mean is None for RMSNorm.
+    """
     if y.shape != resid.shape or y.dtype != resid.dtype:
         raise SratError("resid and y must match")
     desc = norm_desc(resid, norm=norm, eps=eps, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
     rows = resid.shape[0] * resid.shape[1]
-    h = torch.empty_like(resid)
-    u = torch.empty_like(resid)
-    mean = torch.empty(rows, dtype=torch.float32, device=resid.device) if norm == "layernorm" else None
-    rstd = torch.empty(rows, dtype=torch.float32, device=resid.device)
+    if outs is None:
+        h = torch.empty_like(resid)
+        u = torch.empty_like(resid)
+        mean = torch.empty(rows, dtype=torch.float32, device=resid.device) if norm == "layernorm" else None
+        rstd = torch.empty(rows, dtype=torch.float32, device=resid.device)
+    else:
+        h, u, mean, rstd = outs
     _check(lib().srat_sp_norm_fwd(ctypes.byref(desc), _ptr(resid), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(h),
                                   _ptr(u), _ptr(mean), _ptr(rstd), _stream(resid.device)), "srat_sp_norm_fwd")
     return h, u, mean, rstd
 
 
-def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_drop: float = 0.0,
-                seed: int = 0, site: int = 1, seq_offset: int = 0, alias_dy: bool = False,
-                workspace: Optional[torch.Tensor] = None):
-    """dh (= d resid), dy, dgamma, dbeta (None for RMSNorm)."""
-    desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
-    dh = torch.empty_like(h)
-    dy = dh if alias_dy else torch.empty_like(h)
-    hdim = h.shape[2]
-    dgamma = torch.empty(hdim, dtype=torch.float32, device=h.device)
-    dbeta = torch.empty(hdim, dtype=torch.float32, device=h.device) if norm == "layernorm" else None
+def sp_norm_bwd_workspace_bytes(desc: NormDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().srat_sp_norm_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)), "srat_sp_norm_bwd_workspace")
-    ws = workspace if workspace is not None else torch.empty(max(n.value, 1), dtype=torch.uint8, device=h.device)
+    return n.value
+
+
+def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_drop: float = 0.0,
+                seed: int = 0, site: int = 1, seq_offset: int = 0, alias_dy: bool = False,
+                workspace: Optional[torch.Tensor] = None, outs=None):
+    """dh (= d resid), dy, dgamma, dbeta (None for RMSNorm).
+
+    outs: optional preallocated (dh, dy, dgamma, dbeta); dy may be dh when p_drop == 0.
+    """
+    desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    hdim = h.shape[2]
+    if outs is None:
+        dh = torch.empty_like(h)
+        dy = dh if alias_dy else torch.empty_like(h)
+        dgamma = torch.empty(hdim, dtype=torch.float32, device=h.device)
+        dbeta = torch.empty(hdim, dtype=torch.float32, device=h.device) if norm == "layernorm" else None
+    else:
+        dh, dy, dgamma, dbeta = outs
+    if workspace is None:
+        workspace = torch.empty(max(sp_norm_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=h.device)
+    ws = workspace
     _check(lib().srat_sp_norm_bwd(ctypes.byref(desc), _ptr(du), _ptr(dres), _ptr(h), _ptr(gamma), _ptr(mean),
                                   _ptr(rstd), _ptr(dh), _ptr(dy), _ptr(dgamma), _ptr(dbeta), _ptr(ws),
                                   ws.numel(), _stream(h.device)), "srat_sp_norm_bwd")
