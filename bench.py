@@ -61,14 +61,22 @@ def src_hash(*files):
     return h.hexdigest()[:16]
 
 
+_BWD_SRC = ["selective_recompute_attention_attn_amd/csrc/attn_bwd.hip",
+            "selective_recompute_attention_attn_amd/csrc/philox.hpp",
+            "selective_recompute_attention_attn_amd/csrc/common.hpp"]
 KERNEL_SOURCES = {
-    "attn_bwd_bf16": ["selective_recompute_attention_attn_amd/csrc/attn_bwd.hip",
-                      "selective_recompute_attention_attn_amd/csrc/philox.hpp",
-                      "selective_recompute_attention_attn_amd/csrc/common.hpp"],
+    "attn_bwd_dkdv": _BWD_SRC,
+    "attn_bwd_dq": _BWD_SRC,
     "attn_fwd_bf16": ["selective_recompute_attention_attn_amd/csrc/attn_fwd.hip",
                       "selective_recompute_attention_attn_amd/csrc/philox.hpp",
                       "selective_recompute_attention_attn_amd/csrc/common.hpp"],
 }
+
+# Algorithmic FLOPs per score element and head-dim unit of each attention
+# kernel: forward QK^T + PV = 4; backward 10 = QK^T recompute, dP, dV, dK (the
+# dK/dV kernel, 8) + dQ (the dQ kernel, 2; the QK^T and dO V^T it re-does to
+# avoid atomics are not algorithmic work).
+KERNEL_FLOP_UNITS = {"attn_fwd_bf16": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 
 
 def measured_traffic(kernel, workload):
@@ -237,10 +245,10 @@ def main():
     if kernels:
         dom = max(trace, key=lambda k: trace[k][1])
         mean_s = trace[dom][1] / trace[dom][0] * 1e-3
-        work = {"attn_bwd_bf16": ("mfma", attn_flops(a, fwd=False, bwd=True)),
-                "attn_fwd_bf16": ("mfma", attn_flops(a, fwd=True, bwd=False)),
-                "sp_norm_fwd": ("hbm", norm_bytes(n, True)),
-                "sp_norm_bwd": ("hbm", norm_bytes(n, False))}
+        units = a.b * a.hq * a.s * a.s * a.d * (0.5 if a.causal else 1.0)
+        work = {k: ("mfma", units * u) for k, u in KERNEL_FLOP_UNITS.items()}
+        work.update({"sp_norm_fwd": ("hbm", norm_bytes(n, True)),
+                     "sp_norm_bwd": ("hbm", norm_bytes(n, False))})
         if dom in work:
             bound, amount = work[dom]
             if bound == "mfma":
@@ -262,8 +270,9 @@ def main():
         "attn_ms": attn_ms,
         "attn_fwd_tflops": (attn_flops(a, True, False) / (kernels["attn_fwd_bf16"]["mean_us"] * 1e-6) / 1e12
                             if "attn_fwd_bf16" in kernels else None),
-        "attn_bwd_tflops": (attn_flops(a, False, True) / (kernels["attn_bwd_bf16"]["mean_us"] * 1e-6) / 1e12
-                            if "attn_bwd_bf16" in kernels else None),
+        "attn_bwd_tflops": (attn_flops(a, False, True)
+                            / (sum(v["mean_us"] for k, v in kernels.items() if k.startswith("attn_bwd")) * 1e-6)
+                            / 1e12 if "attn_bwd_dkdv" in kernels else None),
         "sp_fwd_gbps": norm_bytes(n, True) / (nf_ms * 1e-3) / 1e9,
         "sp_bwd_gbps": norm_bytes(n, False) / (nb_ms * 1e-3) / 1e9,
         "sp_fwd_frac_of_hbm": norm_bytes(n, True) / (nf_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,

@@ -89,7 +89,7 @@ typedef struct {
   int64_t k_stride[3];    /* ... of K, dK */
   int64_t v_stride[3];    /* ... of V, dV */
   int64_t o_stride[3];    /* ... of O, dO */
-  float scale;            /* softmax scale, normally 1/sqrt(d) */
+  float scale;            /* softmax scale > 0, normally 1/sqrt(d) */
   float p_drop;           /* attention-dropout probability in [0, 1); 0 disables it */
   uint64_t seed;          /* Philox key of the attention dropout */
   int64_t head_offset;    /* global index of local q-head 0 (TP rank * hq) */
@@ -105,9 +105,9 @@ int srat_attn_core_fwd(const srat_attn_desc* desc, const void* q, const void* k,
                        const void* v, void* o, float* lse, void* stream);
 
 /*
- * Workspace bytes srat_attn_core_bwd needs: O(b * s * hq * d) (fp32 dQ
- * accumulator, per-row D = rowsum(dO * O), per-q-head dK/dV partials for
- * grouped-query attention).  Never O(s^2).
+ * Workspace bytes srat_attn_core_bwd needs: the per-row D = rowsum(dO * O)
+ * (4 b hq s bytes) and, for grouped-query attention only, per-q-head fp32
+ * dK / dV partials (8 b s hq d bytes).  Never O(s^2).
  */
 int srat_attn_core_bwd_workspace(const srat_attn_desc* desc, size_t* bytes);
 
@@ -115,7 +115,8 @@ int srat_attn_core_bwd_workspace(const srat_attn_desc* desc, size_t* bytes);
  * Backward with recomputation: rebuilds S = Q K^T * scale, P = exp(S - lse)
  * and the dropout mask instead of reading stored activations, then
  * dV = P_d^T dO, dS = P * (dP - rowsum(dO * O)), dQ = dS K * scale,
- * dK = dS^T Q * scale (summed over each kv-head's q-heads).
+ * dK = dS^T Q * scale (summed over each kv-head's q-heads).  No atomics: the
+ * gradients are bitwise reproducible.
  * q, k, v, o, lse are the forward's inputs/outputs; dout is dL/dO.
  * ws: device workspace of at least srat_attn_core_bwd_workspace() bytes,
  * 256-byte aligned.  dq, dk, dv: outputs with the strides of q, k, v.

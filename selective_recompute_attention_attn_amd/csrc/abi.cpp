@@ -75,7 +75,7 @@ int check_attn(const srat_attn_desc* d) {
   if (d->head_offset < 0 || d->head_offset + d->hq > ((int64_t)1 << 31))
     return fail(SRAT_ERR_INVALID, "head_offset out of range");
   if (!(d->p_drop >= 0.f && d->p_drop < 1.f)) return fail(SRAT_ERR_INVALID, "p_drop %g not in [0, 1)", d->p_drop);
-  if (!std::isfinite(d->scale)) return fail(SRAT_ERR_INVALID, "scale not finite");
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return fail(SRAT_ERR_INVALID, "scale must be finite and > 0");
   const int64_t al = d->dtype == SRAT_BF16 ? 8 : 4;
   const int64_t* st[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
   for (int t = 0; t < 4; ++t)
@@ -111,13 +111,14 @@ srat::AttnParams attn_params(const srat_attn_desc* d) {
 }
 
 struct AttnWs {
-  size_t dq_acc, delta, dk_part, dv_part, total;
+  size_t delta, dk_part, dv_part, total;
 };
+// rowsum(dO * O) per query row, plus per-q-head fp32 dK / dV partials when
+// several q-heads share a kv-head (summed by a final kernel)
 AttnWs attn_ws(const srat_attn_desc* d) {
   AttnWs w{};
   const size_t rows = (size_t)d->b * d->s * d->hq;
   size_t off = 0;
-  w.dq_acc = off; off += align256(rows * d->d * sizeof(float));
   w.delta = off; off += align256(rows * sizeof(float));
   if (d->hq != d->hkv) {
     w.dk_part = off; off += align256(rows * d->d * sizeof(float));
@@ -232,11 +233,10 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.dout = dout;
   p.dq = dq; p.dk = dk; p.dv = dv;
   char* base = static_cast<char*>(ws);
-  p.dq_acc = reinterpret_cast<float*>(base + w.dq_acc);
   p.delta = reinterpret_cast<float*>(base + w.delta);
   if (desc->hq != desc->hkv) {
-    p.dk_part = reinterpret_cast<float*>(base + w.dk_part);
-    p.dv_part = reinterpret_cast<float*>(base + w.dv_part);
+    p.dk_acc = reinterpret_cast<float*>(base + w.dk_part);
+    p.dv_acc = reinterpret_cast<float*>(base + w.dv_part);
   }
   hipError_t e = srat::launch_attn_bwd(p, desc->dtype == SRAT_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core_bwd launch");

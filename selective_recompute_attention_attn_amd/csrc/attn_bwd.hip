@@ -4,7 +4,7 @@
 // (scores, softmax, dropout mask and output) after the forward and re-runs the
 // core in the backward pass ("Reducing Activation Recomputation in Large
 // Transformer Models", LIT-736 record, Key takeaways bullet 4).  Here the
-// re-run is fused into the gradient kernel, tile by tile, so nothing of size
+// re-run is fused into the gradient kernels, tile by tile, so nothing of size
 // s x s is ever written:
 //
 //   S  = Q K^T * scale,  P = exp(S - LSE)          (recomputed)
@@ -13,19 +13,27 @@
 //   dP = dO V^T * M / (1-p),  dS = P * (dP - D),  D = rowsum(dO * O)
 //   dQ = dS K * scale,        dK = dS^T Q * scale
 //
-// Three kernels on one stream:
-//   pre : D = rowsum(dO * O) per query row, zero the fp32 dQ accumulator
-//   main: one workgroup per (128-key block, q-head, batch); 4 waves, wave w
-//         owns keys 32w .. 32w+31 of the block.  It loops over 32-query tiles:
-//         S^T = K Q^T and dP^T = V dO^T with K, V as register-resident MFMA A
-//         operands (rows permuted as in the forward, so one lane holds one
-//         query and 16 consecutive keys: softmax recompute, mask and dS are
-//         lane-local and one Philox call covers 8 keys).  P*M and dS go to LDS
-//         once; dV, dK read them back transposed with ds_read_b64_tr_b16, dQ
-//         reads dS directly and K transposed; dQ is added to the fp32
-//         accumulator with hardware float atomics.
-//   post: dQ accumulator -> dQ (x scale, bf16); grouped-query attention: dK,
-//         dV summed over the q-heads that share a kv-head.
+// Kernels on one stream, no atomics (results are deterministic):
+//   pre : D = rowsum(dO * O) per query row.
+//   dkdv: one workgroup per (128-key block, q-head, batch).  Waves split the
+//         block's keys into four 32-key groups (and, for head dims <= 96, each
+//         64-query tile into two 32-query halves, one wave per pair).  A wave
+//         computes S^T = K Q^T and dP^T = V dO^T with its K, V rows as
+//         register-resident MFMA A operands, rows permuted so that one lane
+//         holds one query and 16 consecutive keys: the softmax recompute, the
+//         mask (one Philox call per 8 keys) and dS are lane-local.  P*M and
+//         dS go through a wave-private LDS tile and come back transposed
+//         (ds_read_b64_tr_b16) as the A operands of dV += (P*M)^T dO and
+//         dK += dS^T Q.  Blocks are launched lowest keys first (the most
+//         queries under a causal mask) and one block per CU, so the dispatcher
+//         balances causal work.
+//   dq  : one workgroup per 128 queries, the forward's shape: it loops over
+//         64-key tiles, recomputes S^T and dP^T, forms dS^T in registers and
+//         accumulates dQ^T += K^T dS^T (K^T through LDS transpose reads).
+//         Re-doing QK^T and dO V^T here costs MFMA work (not counted in the
+//         algorithmic FLOPs) but removes every atomic from the backward.
+//   gqa_sum: grouped-query attention only: dK, dV = sums over the q-heads that
+//         share a kv-head of the per-q-head fp32 partials.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
@@ -33,104 +41,115 @@
 namespace srat {
 namespace {
 
-constexpr int kBNk = 128;      // keys per workgroup
-constexpr int kBMq = 32;       // queries per iteration
-constexpr int kThreads = 256;  // 4 waves
-
-template <int D>
-struct BwdSmem {
-  static constexpr int kS = D + 8;       // row stride of K, Q, dO tiles (bf16)
-  static constexpr int kP = kBNk + 8;    // row stride of the P*M and dS tiles
-  bf16 k[kBNk * kS];
-  bf16 q[kBMq * kS];
-  bf16 dout[kBMq * kS];
-  bf16 pm[kBMq * kP];
-  bf16 ds[kBMq * kP];
-};
+constexpr int kBNk = 128;      // keys per dkdv workgroup
 
 __device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 
-// Two ds_read_b64_tr_b16 of a row-major bf16 tile give the 32x32x16 MFMA
-// operand "lane (i = l%32, h = l/32) holds column c_base + i, rows
-// r_base + 8h .. +7": lane group G = l/16 covers columns c_base + 16*(G%2) ..
-// and rows r_base + 8*(G/2) ...
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int stride, int r_base, int c_base, int lane) {
+// ds_read_b64_tr_b16 pair -> 32x32x16 MFMA operand "lane (i = l%32, h = l/32)
+// holds column c_base + i, rows r_base + 8h .. +7" of a row-major tile; this is
+// the per-lane part of the element offset (lane group G = l/16 covers columns
+// c_base + 16*(G%2) .. and rows r_base + 8*(G/2) ..).
+__device__ __forceinline__ int tr_off32(int stride, int lane) {
   const int grp = lane >> 4, lg = lane & 15;
-  const int r = r_base + 8 * (grp >> 1) + (lg >> 2);
-  const int c = c_base + 16 * (grp & 1) + 4 * (lg & 3);
-  const s16x4 lo = lds_read_tr16(tile + r * stride + c);
-  const s16x4 hi = lds_read_tr16(tile + (r + 4) * stride + c);
+  return (8 * (grp >> 1) + (lg >> 2)) * stride + 16 * (grp & 1) + 4 * (lg & 3);
+}
+__device__ __forceinline__ bf16x8 tr_pair(const bf16* p, int stride) {
+  const s16x4 lo = lds_read_tr16(p);
+  const s16x4 hi = lds_read_tr16(p + 4 * stride);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, bool CAUSAL, bool DROP, bool GQA>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(AttnParams p) {
-  using SM = BwdSmem<D>;
-  constexpr int kS = SM::kS, kP = SM::kP;
+// The keep decision of element r (0..15) of a lane from its two Philox calls
+// (keys 8*g8 .. 8*g8+15 of one query).
+__device__ __forceinline__ bool keep16(const Philox4 (&rnd)[2], int r, uint32_t thr, uint32_t thr_hi) {
+  const uint32_t w = rnd[r >> 3].w[(r & 7) >> 1];
+  return (r & 1) ? (w >= thr_hi) : ((w & 0xFFFFu) >= thr);
+}
+
+// ============================================================== dK, dV
+// Wave-private P*M and dS tiles: 32 queries x 32 keys stored as two unpadded
+// [32 query][16 key] halves (key half h at offset 512*h), so the lanes' 32-byte
+// row writes are contiguous and every 16-lane transpose-read group covers 32
+// consecutive dwords: no bank conflicts on either side.
+constexpr int kWaveTile = 32 * 32;
+
+template <int D, int QH>
+struct DkdvSmem {
+  static constexpr int kS = TileStride<D>::kValue;   // Q / dO tile row stride (bf16)
+  static constexpr int kRows = 32 * QH;              // queries per tile
+  union {
+    struct {
+      bf16 q[kRows * kS];
+      bf16 dout[kRows * kS];
+      bf16 pm[4 * QH][kWaveTile];
+      bf16 ds[4 * QH][kWaveTile];
+    } t;
+    float comb[4][QH == 2 ? 64 * (D / 32) * 16 : 1];   // q-half combine of one accumulator
+  };
+};
+
+// Heads with at most 96 dims: two query halves (8 waves, 2 per SIMD); larger
+// heads: one (4 waves, accumulators in AGPRs).
+template <int D> struct DkdvCfg { static constexpr int kQH = D <= 96 ? 2 : 1; };
+
+template <int D, bool CAUSAL, bool DROP, bool PART>
+__global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel(AttnParams p) {
+  constexpr int QH = DkdvCfg<D>::kQH;
+  using SM = DkdvSmem<D, QH>;
+  constexpr int kS = SM::kS, kRows = SM::kRows;
+  constexpr int kThreads = 256 * QH;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kTileChunks = kBMq * D / 8;                       // 16-byte chunks per Q or dO tile
+  constexpr int kTileChunks = kRows * D / 8;
   constexpr int kTileLoads = (kTileChunks + kThreads - 1) / kThreads;
   __shared__ SM sm;
 
-  const int nkb = (p.s + kBNk - 1) / kBNk;
-  const int bh = blockIdx.x % (p.b * p.hq);
-  const int kblk = (int)(blockIdx.x / (p.b * p.hq));   // ascending: most work first when causal
+  const int nbh = p.b * p.hq;
+  const int kblk = (int)(blockIdx.x / nbh);          // ascending: most queries first when causal
+  const int bh = blockIdx.x % nbh;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kg = wv & 3, qh = wv >> 2;                // key group, query half
   const int half = lane >> 5, col = lane & 31;
   const int k0 = kblk * kBNk;
-  const int kw0 = k0 + 32 * wv;          // first key of this wave
-  (void)nkb;
+  const int kw0 = k0 + 32 * kg;                       // first key of this wave
 
   const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
   const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
   const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
   const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
   const int64_t row0 = ((int64_t)bb * p.hq + hh_q) * p.s;
-  float* dqa = p.dq_acc + ((int64_t)bb * p.s * p.hq + hh_q) * D;   // [b, s, hq, d] contiguous
 
-  // K block -> LDS (row-major, for the dQ operand)
-#pragma unroll
-  for (int it = 0; it < kBNk * D / 8 / kThreads; ++it) {
-    const int x = tid + kThreads * it;
-    const int r = x / (D / 8), c8 = x % (D / 8);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (k0 + r < p.s) w = *reinterpret_cast<const uint4*>(kp + (int64_t)(k0 + r) * p.sk_s + 8 * c8);
-    *reinterpret_cast<uint4*>(&sm.k[r * kS + 8 * c8]) = w;
-  }
   // K, V rows of this wave as MFMA A operands (rows permuted)
   bf16x8 kreg[kDC], vreg[kDC];
   {
     const int key = kw0 + perm32(col);
+    const bool ok = key < p.s;
+    const int64_t ko = (int64_t)(ok ? key : 0) * p.sk_s + 8 * half;
+    const int64_t vo = (int64_t)(ok ? key : 0) * p.sv_s + 8 * half;
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
-      if (key < p.s) {
-        kreg[c] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * p.sk_s + 16 * c + 8 * half);
-        vreg[c] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * p.sv_s + 16 * c + 8 * half);
-      } else {
-        kreg[c] = bf16x8{};
-        vreg[c] = bf16x8{};
-      }
+      const uint4 a = *reinterpret_cast<const uint4*>(kp + ko + 16 * c);
+      const uint4 b = *reinterpret_cast<const uint4*>(vp + vo + 16 * c);
+      kreg[c] = __builtin_bit_cast(bf16x8, ok ? a : make_uint4(0, 0, 0, 0));
+      vreg[c] = __builtin_bit_cast(bf16x8, ok ? b : make_uint4(0, 0, 0, 0));
     }
   }
-
   f32x16 dv_acc[kDB], dk_acc[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
 
-  const int nqt = (p.s + kBMq - 1) / kBMq;
-  const int qt0 = CAUSAL ? k0 / kBMq : 0;
+  const int nqt = (p.s + kRows - 1) / kRows;
+  const int qt0 = CAUSAL ? k0 / kRows : 0;
   uint4 qpre[kTileLoads], dpre[kTileLoads];
   auto prefetch = [&](int qt) {
 #pragma unroll
     for (int it = 0; it < kTileLoads; ++it) {
       const int x = tid + kThreads * it;
       const int r = x / (D / 8), c8 = x % (D / 8);
-      const int qrow = qt * kBMq + r;
+      const int qrow = qt * kRows + r;
       qpre[it] = dpre[it] = make_uint4(0, 0, 0, 0);
       if (x < kTileChunks && qrow < p.s) {
         qpre[it] = *reinterpret_cast<const uint4*>(qp + (int64_t)qrow * p.sq_s + 8 * c8);
@@ -144,112 +163,122 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(AttnParams p
       const int x = tid + kThreads * it;
       if (x < kTileChunks) {
         const int r = x / (D / 8), c8 = x % (D / 8);
-        *reinterpret_cast<uint4*>(&sm.q[r * kS + 8 * c8]) = qpre[it];
-        *reinterpret_cast<uint4*>(&sm.dout[r * kS + 8 * c8]) = dpre[it];
+        *reinterpret_cast<uint4*>(&sm.t.q[r * kS + 8 * c8]) = qpre[it];
+        *reinterpret_cast<uint4*>(&sm.t.dout[r * kS + 8 * c8]) = dpre[it];
       }
     }
   };
 
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
-  if (qt0 < nqt) prefetch(qt0);
+  const uint32_t thr_hi = p.thresh << 16;
+  const int q_row = (32 * qh + col) * kS + 8 * half;   // this lane's Q / dO row (B operands)
+  const int w_row = 512 * half + 16 * col;             // this lane's 16 keys in the wave tiles
+  // (P*M)^T, dS^T A operands: lane group G reads key half G%2, query rows
+  // 8*(G/2) + (lg/4) (+4), keys 4*(lg%4) .. +3 of that half
+  const int tr_w = 512 * ((lane >> 4) & 1) + (8 * (lane >> 5) + ((lane & 15) >> 2)) * 16 + 4 * (lane & 3);
+  const int tr_s = tr_off32(kS, lane) + 32 * qh * kS;  // dO, Q rows of this query half (B operands)
+  bf16* pmt = sm.t.pm[wv];
+  bf16* dst = sm.t.ds[wv];
+
+  prefetch(qt0);
   for (int qt = qt0; qt < nqt; ++qt) {
     __syncthreads();
     stash();
     __syncthreads();
-    if (qt + 1 < nqt) prefetch(qt + 1);
-    const int qi = qt * kBMq + col;       // this lane's query
+    const int q0 = qt * kRows + 32 * qh;              // first query of this wave
+    const int qi = q0 + col;
     const bool qvalid = qi < p.s;
     const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
     const float dlt = qvalid ? p.delta[row0 + qi] : 0.f;
-    // whole wave above the diagonal of this tile: its P and dS are zero
-    const bool dead = (CAUSAL && kw0 > qt * kBMq + kBMq - 1) || kw0 >= p.s;
 
-    float pmv[16], dsv[16];
-    if (!dead) {
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      const bf16* qrow = &sm.q[col * kS + 8 * half];
-      const bf16* drow = &sm.dout[col * kS + 8 * half];
+    // S^T = K Q^T and dP^T = V dO^T (raw, 32 keys x 32 queries)
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-        sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(qrow + 16 * c), sacc);
-        pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(drow + 16 * c), pacc);
-      }
-      uint32_t bits = 0xFFFFu;
+    for (int c = 0; c < kDC; ++c) {
+      sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&sm.t.q[q_row + 16 * c]), sacc);
+      pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&sm.t.dout[q_row + 16 * c]), pacc);
+    }
+    if (qt + 1 < nqt) prefetch(qt + 1);
+
+    // recompute P, regenerate the mask, P*M and dS packed to bf16 pairs
+    uint32_t pmw[8], dsw[8];
+    const bool dead = (CAUSAL && kw0 > q0 + 31) || kw0 >= p.s;   // the whole 32x32 block is masked
+    if (!dead) {
+      const bool edge = (kw0 + 32 > p.s) || (CAUSAL && kw0 + 31 > q0) || (q0 + 32 > p.s);
+      Philox4 rnd[2];
       if (DROP) {
         const uint32_t g8 = (uint32_t)((kw0 + 16 * half) >> 3);
-        bits = attn_keep8(p.k0, p.k1, (uint32_t)bb, hg, (uint32_t)qi, g8, p.thresh) |
-               (attn_keep8(p.k0, p.k1, (uint32_t)bb, hg, (uint32_t)qi, g8 + 1, p.thresh) << 8);
+        rnd[0] = philox4x32_10(g8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+        rnd[1] = philox4x32_10(g8 + 1, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
       }
-      const bool edge = (kw0 + 32 > p.s) || (CAUSAL && kw0 + 31 > qt * kBMq) || !qvalid;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(sacc[r] * p.scale_log2 - lse2);
-        if (edge) {
-          const int key = kw0 + 16 * half + r;
-          if (key >= p.s || (CAUSAL && key > qi) || !qvalid) pv = 0.f;
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float pk[2], dd[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * r2 + e;
+          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
+          if (edge) {
+            const int key = kw0 + 16 * half + r;
+            if (key >= p.s || (CAUSAL && key > qi) || !qvalid) pv = 0.f;
+          }
+          const bool keep = DROP ? keep16(rnd, r, p.thresh, thr_hi) : true;
+          pk[e] = keep ? pv : 0.f;
+          dd[e] = pv * fmaf(keep ? pacc[r] : 0.f, p.inv_keep, -dlt);
         }
-        const bool keep = (bits >> r) & 1u;
-        pmv[r] = keep ? pv : 0.f;
-        dsv[r] = pv * ((keep ? pacc[r] * p.inv_keep : 0.f) - dlt);
+        pmw[r2] = pack_bf16x2(pk[0], pk[1]);
+        dsw[r2] = pack_bf16x2(dd[0], dd[1]);
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pmv[r] = dsv[r] = 0.f;
+      for (int r2 = 0; r2 < 8; ++r2) pmw[r2] = dsw[r2] = 0u;
     }
-    // P*M and dS rows of this lane's query: keys 32w + 16*half .. +15 of the block
-    {
-      uint4 w0, w1;
-      w0.x = pack_bf16x2(pmv[0], pmv[1]);   w0.y = pack_bf16x2(pmv[2], pmv[3]);
-      w0.z = pack_bf16x2(pmv[4], pmv[5]);   w0.w = pack_bf16x2(pmv[6], pmv[7]);
-      w1.x = pack_bf16x2(pmv[8], pmv[9]);   w1.y = pack_bf16x2(pmv[10], pmv[11]);
-      w1.z = pack_bf16x2(pmv[12], pmv[13]); w1.w = pack_bf16x2(pmv[14], pmv[15]);
-      uint4* dst = reinterpret_cast<uint4*>(&sm.pm[col * kP + 32 * wv + 16 * half]);
-      dst[0] = w0;
-      dst[1] = w1;
-      w0.x = pack_bf16x2(dsv[0], dsv[1]);   w0.y = pack_bf16x2(dsv[2], dsv[3]);
-      w0.z = pack_bf16x2(dsv[4], dsv[5]);   w0.w = pack_bf16x2(dsv[6], dsv[7]);
-      w1.x = pack_bf16x2(dsv[8], dsv[9]);   w1.y = pack_bf16x2(dsv[10], dsv[11]);
-      w1.z = pack_bf16x2(dsv[12], dsv[13]); w1.w = pack_bf16x2(dsv[14], dsv[15]);
-      dst = reinterpret_cast<uint4*>(&sm.ds[col * kP + 32 * wv + 16 * half]);
-      dst[0] = w0;
-      dst[1] = w1;
-    }
-    lds_fence();   // this wave's own P*M / dS columns are read back below
+    *reinterpret_cast<uint4*>(&pmt[w_row]) = make_uint4(pmw[0], pmw[1], pmw[2], pmw[3]);
+    *reinterpret_cast<uint4*>(&pmt[w_row + 8]) = make_uint4(pmw[4], pmw[5], pmw[6], pmw[7]);
+    *reinterpret_cast<uint4*>(&dst[w_row]) = make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]);
+    *reinterpret_cast<uint4*>(&dst[w_row + 8]) = make_uint4(dsw[4], dsw[5], dsw[6], dsw[7]);
+    lds_fence();   // the wave reads its own tiles back transposed
 
-    if (!dead) {
-      // dV_w += (P*M)^T dO ;  dK_w += dS^T Q   (contraction over the 32 queries)
+    // dV += (P*M)^T dO ;  dK += dS^T Q   (contraction over the wave's 32 queries)
 #pragma unroll
-      for (int st = 0; st < kBMq / 16; ++st) {
-        const bf16x8 apm = tr_operand(sm.pm, kP, 16 * st, 32 * wv, lane);
-        const bf16x8 ads = tr_operand(sm.ds, kP, 16 * st, 32 * wv, lane);
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 apm = tr_pair(&pmt[16 * st * 16 + tr_w], 16);
+      const bf16x8 ads = tr_pair(&dst[16 * st * 16 + tr_w], 16);
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          dv_acc[db] = mfma32(apm, tr_operand(sm.dout, kS, 16 * st, 32 * db, lane), dv_acc[db]);
-          dk_acc[db] = mfma32(ads, tr_operand(sm.q, kS, 16 * st, 32 * db, lane), dk_acc[db]);
-        }
-      }
-    }
-    __syncthreads();   // every wave's dS is in LDS
-
-    // dQ (32 queries x D) = dS (32 x 128 keys) K (128 x D); wave w takes d blocks w, w+4, ...
-    const int kend = min(kBNk, p.s - k0);           // keys of the block that exist
-    const int nst = CAUSAL ? min((kend + 15) / 16, (qt * kBMq + kBMq - 1 - k0) / 16 + 1) : (kend + 15) / 16;
-    for (int db = wv; db < kDB; db += 4) {
-      f32x16 qacc = f32x16{};
-      for (int st = 0; st < nst; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.ds[col * kP + 16 * st + 8 * half]);
-        qacc = mfma32(a, tr_operand(sm.k, kS, 16 * st, 32 * db, lane), qacc);
-      }
-      // lane holds d = 32db + col, queries 8*(r/4) + 4*half + r%4 of the tile
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = qt * kBMq + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (qq < p.s) unsafeAtomicAdd(dqa + (int64_t)qq * p.hq * D + 32 * db + col, qacc[r]);
+      for (int db = 0; db < kDB; ++db) {
+        dv_acc[db] = mfma32(apm, tr_pair(&sm.t.dout[16 * st * kS + tr_s + 32 * db], kS), dv_acc[db]);
+        dk_acc[db] = mfma32(ads, tr_pair(&sm.t.q[16 * st * kS + tr_s + 32 * db], kS), dk_acc[db]);
       }
     }
   }
 
-  // epilogue: lane holds d = 32db + col, keys kw0 + 8*(r/4) + 4*half + r%4
+  // two query halves: the second adds its share into the first through LDS
+  if (QH == 2) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      __syncthreads();
+      if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sm.comb[kg][(db * 16 + r) * 64 + lane] = which ? dk_acc[db][r] : dv_acc[db][r];
+      }
+      __syncthreads();
+      if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = sm.comb[kg][(db * 16 + r) * 64 + lane];
+            if (which) dk_acc[db][r] += x;
+            else dv_acc[db][r] += x;
+          }
+      }
+    }
+    if (qh == 1) return;
+  }
+
+  // store: lane holds d = 32db + col, keys kw0 + 8*(r/4) + 4*half + r%4
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
 #pragma unroll
@@ -259,10 +288,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(AttnParams p
       const float dvv = dv_acc[db][r] * p.inv_keep;
       const float dkv = dk_acc[db][r] * p.scale;
       const int dcol = 32 * db + col;
-      if (GQA) {
+      if (PART) {
         const int64_t o = (((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
-        p.dv_part[o] = dvv;
-        p.dk_part[o] = dkv;
+        p.dv_acc[o] = dvv;
+        p.dk_acc[o] = dkv;
       } else {
         static_cast<bf16*>(p.dv)[bb * p.sv_b + (int64_t)key * p.sv_s + g * p.sv_h + dcol] = (bf16)dvv;
         static_cast<bf16*>(p.dk)[bb * p.sk_b + (int64_t)key * p.sk_s + g * p.sk_h + dcol] = (bf16)dkv;
@@ -271,8 +300,181 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(AttnParams p
   }
 }
 
-// D = rowsum(dO * O) for every (b, q-head, query) row; zero the dQ accumulator.
-// 8 lanes per row, lane t takes 8-element chunks t, t+8, ...
+// ============================================================== dQ
+constexpr int kQM = 128;       // queries per dq workgroup
+constexpr int kQN = 64;        // keys per K/V tile
+
+template <int D>
+struct DqSmem {
+  static constexpr int kStride = TileStride<D>::kValue;
+  bf16 k[kQN * kStride];
+  bf16 v[kQN * kStride];
+};
+
+__device__ __forceinline__ int causal_tile(int rank, int nqt) {
+  const int h = (nqt + 1) / 2;
+  return rank < h ? nqt - 1 - rank : rank - h;
+}
+
+template <int D> struct DqOcc { static constexpr int kWavesPerEU = D <= 96 ? 2 : 1; };
+
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel(AttnParams p) {
+  constexpr int kStride = DqSmem<D>::kStride;
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kLoads = D / 32;
+  __shared__ DqSmem<D> sm;
+
+  const int nqt = (p.s + kQM - 1) / kQM;
+  const int nbh = p.b * p.hq;
+  const int bh = blockIdx.x % nbh;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  const int hh_q = bh % p.hq, bb = bh / p.hq;
+  const int g = hh_q / (p.hq / p.hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int q0 = qt * kQM;
+  const int qw = q0 + 32 * wv;
+  const int qi = qw + col;
+  const bool qvalid = qi < p.s;
+
+  const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
+  const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
+  const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
+  const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
+  const int64_t row0 = ((int64_t)bb * p.hq + hh_q) * p.s;
+
+  // Q^T and dO^T B operands: lane (col, half) holds row qi, d = 16c + 8*half ..
+  bf16x8 qreg[kDC], doreg[kDC];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) qreg[c] = doreg[c] = bf16x8{};
+  if (qvalid) {
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
+      doreg[c] = *reinterpret_cast<const bf16x8*>(dop + (int64_t)qi * p.so_s + 16 * c + 8 * half);
+    }
+  }
+  const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
+  const float dlt = qvalid ? p.delta[row0 + qi] : 0.f;
+
+  f32x16 qacc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) qacc[db] = f32x16{};
+
+  const int nkt_all = (p.s + kQN - 1) / kQN;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + kQM + kQN - 1) / kQN) : nkt_all;
+  uint4 kpre[kLoads], vpre[kLoads];
+  auto prefetch = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int x = tid + 256 * it;
+      const int key = kt * kQN + x / (D / 8);
+      const int c8 = x % (D / 8);
+      kpre[it] = vpre[it] = make_uint4(0, 0, 0, 0);
+      if (key < p.s) {
+        kpre[it] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * p.sk_s + 8 * c8);
+        vpre[it] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.sv_s + 8 * c8);
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int x = tid + 256 * it;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<uint4*>(&sm.k[r * kStride + 8 * c8]) = kpre[it];
+      *reinterpret_cast<uint4*>(&sm.v[r * kStride + 8 * c8]) = vpre[it];
+    }
+  };
+
+  const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const uint32_t thr_hi = p.thresh << 16;
+  const int krow = perm32(col) * kStride + 8 * half;
+  const int grp = lane >> 4, lg = lane & 15;
+  const int ktr = (16 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
+
+  prefetch(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (kt + 1 < nkt) prefetch(kt + 1);
+    const int key0 = kt * kQN;
+    if (CAUSAL && key0 > qw + 31) continue;   // whole tile above this wave's diagonal
+
+    // S^T = K Q^T, dP^T = V dO^T for two 32-key blocks
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = pacc[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        const int o = 32 * kb * kStride + krow + 16 * c;
+        sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.k[o]), qreg[c], sacc[kb]);
+        pacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.v[o]), doreg[c], pacc[kb]);
+      }
+    }
+
+    // dS^T = P * (dP * M / (1-p) - D) as bf16 B operands (step c = block c/2, regs 8*(c%2)..)
+    const bool edge = (key0 + kQN > p.s) || (CAUSAL && key0 + kQN - 1 > qw) || !qvalid;
+    bf16x8 dsop[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Philox4 rnd[2];
+      if (DROP) {
+        const uint32_t g8 = (uint32_t)((key0 + 32 * kb + 16 * half) >> 3);
+        rnd[0] = philox4x32_10(g8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+        rnd[1] = philox4x32_10(g8 + 1, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -lse2));
+        if (edge) {
+          const int key = key0 + 32 * kb + 16 * half + r;
+          if (key >= p.s || (CAUSAL && key > qi) || !qvalid) pv = 0.f;
+        }
+        const bool keep = DROP ? keep16(rnd, r, p.thresh, thr_hi) : true;
+        const float d = pv * fmaf(keep ? pacc[kb][r] : 0.f, p.inv_keep, -dlt);
+        dsop[2 * kb + (r >> 3)][r & 7] = (bf16)d;
+      }
+    }
+
+    // dQ^T += K^T dS^T; K^T operand through LDS transpose reads
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kStride + ktr;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const s16x4 lo = lds_read_tr16(&sm.k[r0 + 32 * db]);
+        const s16x4 hi = lds_read_tr16(&sm.k[r0 + 4 * kStride + 32 * db]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        qacc[db] = mfma32(a, dsop[c], qacc[db]);
+      }
+    }
+  }
+
+  // dQ = dQ^T * scale; lane holds query qi, d = 32db + 8a + 4*half + j
+  if (qvalid) {
+    bf16* dq = static_cast<bf16*>(p.dq) + bb * p.sq_b + (int64_t)qi * p.sq_s + hh_q * p.sq_h;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 w;
+        w.x = pack_bf16x2(qacc[db][4 * a + 0] * p.scale, qacc[db][4 * a + 1] * p.scale);
+        w.y = pack_bf16x2(qacc[db][4 * a + 2] * p.scale, qacc[db][4 * a + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dq + 32 * db + 8 * a + 4 * half) = w;
+      }
+    }
+  }
+}
+
+// ============================================================== pre / gqa_sum
+// D = rowsum(dO * O) for every (b, q-head, query) row: 8 lanes per row, lane t
+// takes 8-element chunks t, t+8, ...
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnParams p) {
   const int64_t rows = (int64_t)p.b * p.s * p.hq;            // ordered (b, s, hq)
@@ -285,15 +487,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnParams p) {
     const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
     const bf16* o = static_cast<const bf16*>(p.o) + bb * p.so_b + (int64_t)i * p.so_s + hh * p.so_h;
     const bf16* d = static_cast<const bf16*>(p.dout) + bb * p.so_b + (int64_t)i * p.so_s + hh * p.so_h;
-    float* z = p.dq_acc + row * D;
     for (int c = t; c < D / 8; c += 8) {
       const uint4 a = *reinterpret_cast<const uint4*>(o + 8 * c);
       const uint4 b = *reinterpret_cast<const uint4*>(d + 8 * c);
       acc += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
              bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
              bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
-      reinterpret_cast<float4*>(z + 8 * c)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      reinterpret_cast<float4*>(z + 8 * c)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   acc += __shfl_xor(acc, 1, kWave);
@@ -307,60 +506,52 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnParams p) {
   }
 }
 
-// dQ = acc * scale -> bf16; GQA: dK, dV = sum of the group's per-q-head partials.
-template <int D, bool GQA>
-__global__ __launch_bounds__(256) void attn_bwd_post_kernel(AttnParams p) {
-  const int64_t nq = (int64_t)p.b * p.s * p.hq * (D / 8);    // 8-element chunks of dQ
-  const int64_t nk = GQA ? (int64_t)p.b * p.s * p.hkv * (D / 8) : 0;
+// Grouped-query attention: dK, dV of a kv-head = sums over its q-heads' fp32
+// partials ([b, s, hq, d]), written as bf16 in 8-element chunks.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_gqa_sum_kernel(AttnParams p) {
+  const int64_t nk = (int64_t)p.b * p.s * p.hkv * (D / 8);
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x < nq) {
-    const int c8 = (int)(x % (D / 8));
-    const int64_t row = x / (D / 8);                           // (b, s, hq)
-    const int hh = (int)(row % p.hq);
-    const int64_t bs = row / p.hq;
-    const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
-    const float* a = p.dq_acc + row * D + 8 * c8;
-    const float4 u = reinterpret_cast<const float4*>(a)[0];
-    const float4 v = reinterpret_cast<const float4*>(a)[1];
-    uint4 w;
-    w.x = pack_bf16x2(u.x * p.scale, u.y * p.scale);
-    w.y = pack_bf16x2(u.z * p.scale, u.w * p.scale);
-    w.z = pack_bf16x2(v.x * p.scale, v.y * p.scale);
-    w.w = pack_bf16x2(v.z * p.scale, v.w * p.scale);
-    *reinterpret_cast<uint4*>(static_cast<bf16*>(p.dq) + bb * p.sq_b + (int64_t)i * p.sq_s + hh * p.sq_h + 8 * c8) = w;
-  } else if (GQA && x < nq + nk) {
-    const int64_t y = x - nq;
-    const int c8 = (int)(y % (D / 8));
-    const int64_t row = y / (D / 8);                           // (b, s, hkv)
-    const int gg = (int)(row % p.hkv);
-    const int64_t bs = row / p.hkv;
-    const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
-    const int grp = p.hq / p.hkv;
-    float sk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < grp; ++j) {
-      const int64_t o = (((int64_t)bb * p.s + i) * p.hq + gg * grp + j) * D + 8 * c8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sk[e] += p.dk_part[o + e];
-        sv[e] += p.dv_part[o + e];
-      }
-    }
-    uint4 wk, wv;
-    wk.x = pack_bf16x2(sk[0], sk[1]); wk.y = pack_bf16x2(sk[2], sk[3]);
-    wk.z = pack_bf16x2(sk[4], sk[5]); wk.w = pack_bf16x2(sk[6], sk[7]);
-    wv.x = pack_bf16x2(sv[0], sv[1]); wv.y = pack_bf16x2(sv[2], sv[3]);
-    wv.z = pack_bf16x2(sv[4], sv[5]); wv.w = pack_bf16x2(sv[6], sv[7]);
-    *reinterpret_cast<uint4*>(static_cast<bf16*>(p.dk) + bb * p.sk_b + (int64_t)i * p.sk_s + gg * p.sk_h + 8 * c8) = wk;
-    *reinterpret_cast<uint4*>(static_cast<bf16*>(p.dv) + bb * p.sv_b + (int64_t)i * p.sv_s + gg * p.sv_h + 8 * c8) = wv;
+  if (x >= 2 * nk) return;
+  const bool is_v = x >= nk;
+  const int64_t y = is_v ? x - nk : x;
+  const int c8 = (int)(y % (D / 8));
+  const int64_t row = y / (D / 8);                           // (b, s, hkv)
+  const int gg = (int)(row % p.hkv);
+  const int64_t bs = row / p.hkv;
+  const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
+  const int grp = p.hq / p.hkv;
+  const float* src = (is_v ? p.dv_acc : p.dk_acc) + (bs * p.hq + (int64_t)gg * grp) * D + 8 * c8;
+  float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < grp; ++j) {
+    const float4 u = reinterpret_cast<const float4*>(src + (int64_t)j * D)[0];
+    const float4 v = reinterpret_cast<const float4*>(src + (int64_t)j * D)[1];
+    a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+    a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
   }
+  uint4 w;
+  w.x = pack_bf16x2(a[0], a[1]); w.y = pack_bf16x2(a[2], a[3]);
+  w.z = pack_bf16x2(a[4], a[5]); w.w = pack_bf16x2(a[6], a[7]);
+  bf16* dst = is_v ? static_cast<bf16*>(p.dv) + bb * p.sv_b + (int64_t)i * p.sv_s + gg * p.sv_h
+                   : static_cast<bf16*>(p.dk) + bb * p.sk_b + (int64_t)i * p.sk_s + gg * p.sk_h;
+  *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
 }
 
 template <int D, bool CAUSAL, bool DROP>
-hipError_t main_launch(const AttnParams& p, hipStream_t st) {
-  const int nkb = (p.s + kBNk - 1) / kBNk;
-  const dim3 grid((unsigned)(nkb * p.hq * p.b));
-  if (p.hq != p.hkv) attn_bwd_bf16_kernel<D, CAUSAL, DROP, true><<<grid, kThreads, 0, st>>>(p);
-  else attn_bwd_bf16_kernel<D, CAUSAL, DROP, false><<<grid, kThreads, 0, st>>>(p);
+hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
+  const bool part = p.hq != p.hkv;
+  {
+    TraceScope ts("attn_bwd_dkdv", st);
+    const dim3 grid((unsigned)(((p.s + kBNk - 1) / kBNk) * p.hq * p.b));
+    const int threads = 256 * DkdvCfg<D>::kQH;
+    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
+    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TraceScope ts("attn_bwd_dq", st);
+  const dim3 grid((unsigned)(((p.s + kQM - 1) / kQM) * p.hq * p.b));
+  attn_bwd_dq_kernel<D, CAUSAL, DROP><<<grid, 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -373,20 +564,14 @@ hipError_t bwd_launch_d(const AttnParams& p, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    TraceScope ts("attn_bwd_bf16", st);
-    const bool drop = p.thresh != 0;
-    hipError_t e;
-    if (p.causal) e = drop ? main_launch<D, true, true>(p, st) : main_launch<D, true, false>(p, st);
-    else e = drop ? main_launch<D, false, true>(p, st) : main_launch<D, false, false>(p, st);
-    if (e != hipSuccess) return e;
-  }
-  TraceScope ts("attn_bwd_post", st);
-  const bool gqa = p.hq != p.hkv;
-  const int64_t n = rows * (D / 8) + (gqa ? (int64_t)p.b * p.s * p.hkv * (D / 8) : 0);
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (gqa) attn_bwd_post_kernel<D, true><<<blocks, 256, 0, st>>>(p);
-  else attn_bwd_post_kernel<D, false><<<blocks, 256, 0, st>>>(p);
+  const bool drop = p.thresh != 0;
+  hipError_t e;
+  if (p.causal) e = drop ? bwd_main<D, true, true>(p, st) : bwd_main<D, true, false>(p, st);
+  else e = drop ? bwd_main<D, false, true>(p, st) : bwd_main<D, false, false>(p, st);
+  if (e != hipSuccess || p.hq == p.hkv) return e;
+  TraceScope ts("attn_bwd_gqa_sum", st);
+  const int64_t n = 2 * (int64_t)p.b * p.s * p.hkv * (D / 8);
+  attn_bwd_gqa_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -36,10 +36,13 @@ namespace {
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kThreads = 256;  // 4 waves
+// The running max only moves when a tile's max exceeds it by more than this
+// (log2 units): probabilities stay <= 2^8, and the O / l rescale is rare.
+constexpr float kMaxSlack = 8.0f;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int kStride = D + 8;   // bf16 elements per LDS row (16 B pad)
+  static constexpr int kStride = TileStride<D>::kValue;
   bf16 k[kBN * kStride];
   bf16 v[kBN * kStride];
 };
@@ -48,6 +51,14 @@ struct FwdSmem {
 // 8a + 4hh + jj hold keys 16hh + 4a + jj, so output register r of lane half hh
 // is key 16hh + r.
 __device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// Causal q-tile order: the first half of the grid runs the longest tiles
+// first, the second half the shortest first, so two workgroups that share a
+// CU (block i and block i + grid/2) carry equal work.
+__device__ __forceinline__ int causal_tile(int rank, int nqt) {
+  const int h = (nqt + 1) / 2;
+  return rank < h ? nqt - 1 - rank : rank - h;
+}
 
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p) {
@@ -58,8 +69,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   __shared__ FwdSmem<D> sm;
 
   const int nqt = (p.s + kBM - 1) / kBM;
-  const int bh = blockIdx.x % (p.b * p.hq);
-  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / (p.b * p.hq)) : (int)(blockIdx.x / (p.b * p.hq));
+  const int nbh = p.b * p.hq;
+  const int bh = blockIdx.x % nbh;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int qt = CAUSAL ? causal_tile(rank, nqt) : rank;
   const int hh_q = bh % p.hq;
   const int bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
@@ -76,22 +89,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   // Q^T B operand: lane (col, half) holds Q[qi][16c + 8*half .. +7]
   bf16x8 qreg[kDC];
 #pragma unroll
-  for (int c = 0; c < kDC; ++c) {
-    if (qi < p.s)
+  for (int c = 0; c < kDC; ++c) qreg[c] = bf16x8{};
+  if (qi < p.s) {
+#pragma unroll
+    for (int c = 0; c < kDC; ++c)
       qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
-    else
-      qreg[c] = bf16x8{};
   }
 
   f32x16 oacc[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_use = -INFINITY;   // running max, log2-scaled units
+  float l_run = 0.f;         // lane-partial row sum (this lane's keys)
 
   const int nkt_all = (p.s + kBN - 1) / kBN;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
 
-  // global -> register prefetch of one K/V tile: chunk x = tid + 256*it
+  // global -> register prefetch of one K/V tile: 16-byte chunk x = tid + 256*it
   uint4 kpre[kLoads], vpre[kLoads];
   auto prefetch = [&](int kt) {
 #pragma unroll
@@ -99,12 +113,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
       const int x = tid + kThreads * it;
       const int key = kt * kBN + x / (D / 8);
       const int c8 = x % (D / 8);
+      kpre[it] = make_uint4(0, 0, 0, 0);
+      vpre[it] = make_uint4(0, 0, 0, 0);
       if (key < p.s) {
         kpre[it] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * p.sk_s + 8 * c8);
         vpre[it] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.sv_s + 8 * c8);
-      } else {
-        kpre[it] = make_uint4(0, 0, 0, 0);
-        vpre[it] = make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -119,6 +132,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   };
 
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const uint32_t thr_hi = p.thresh << 16;
+  const float c2 = p.scale_log2;
+  // LDS element offsets that do not change across tiles
+  const int krow = perm32(col) * kStride + 8 * half;
+  const int grp = lane >> 4, lg = lane & 15;
+  const int vrow = (16 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
+
   prefetch(0);
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
@@ -128,65 +148,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
     const int key0 = kt * kBN;
     if (CAUSAL && key0 > qw + 31) continue;   // whole tile above this wave's diagonal
 
-    // ---- S^T = K Q^T for two 32-key blocks
+    // ---- S^T = K Q^T (raw scores) for two 32-key blocks
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
-      const bf16* krow = &sm.k[(32 * kb + perm32(col)) * kStride + 8 * half];
 #pragma unroll
       for (int c = 0; c < kDC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[32 * kb * kStride + krow + 16 * c]);
         sacc[kb] = mfma32(a, qreg[c], sacc[kb]);
       }
     }
 
-    // ---- scale, mask, online softmax (lane-local: one query, 32 keys)
+    // ---- mask, tile max (raw units; the scale is positive)
     const bool edge = (key0 + kBN > p.s) || (CAUSAL && key0 + kBN - 1 > qw);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * p.scale_log2;
         if (edge) {
           const int key = key0 + 32 * kb + 16 * half + r;
-          if (key >= p.s || (CAUSAL && key > qi)) x = -INFINITY;
+          if (key >= p.s || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
         }
-        sacc[kb][r] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, sacc[kb][r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c2;
+    const bool grow = mx > m_use + kMaxSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_use;
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);   // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
+      m_use = m_new;
+    }
+    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+
+    // ---- p = exp2(s * c - m); row-sum of the undropped values
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -msub));
         sacc[kb][r] = e;
         lsum += e;
       }
     }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
+    l_run += lsum;
 
-    // ---- dropout: zero the dropped probabilities (scale applied in the epilogue)
+    // ---- dropout: zero the dropped probabilities (1/(1-p) applied in the epilogue)
     if (DROP) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int gh = 0; gh < 2; ++gh) {
           const uint32_t grp8 = (uint32_t)((key0 + 32 * kb + 16 * half + 8 * gh) >> 3);
-          const uint32_t bits = attn_keep8(p.k0, p.k1, (uint32_t)bb, hg, (uint32_t)qi, grp8, p.thresh);
+          const Philox4 rnd = philox4x32_10(grp8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (!((bits >> e) & 1u)) sacc[kb][8 * gh + e] = 0.f;
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = rnd.w[e >> 1];
+            const bool keep = (e & 1) ? (w >= thr_hi) : ((w & 0xFFFFu) >= p.thresh);
+            sacc[kb][8 * gh + e] = keep ? sacc[kb][8 * gh + e] : 0.f;
+          }
         }
       }
     }
@@ -202,15 +228,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
     // ---- O^T += V^T P^T; V^T operand via LDS transpose reads:
     // lane group G = lane/16 covers d = 32db + 16*(G%2) + (0..15) and the keys
     // 32*kb + 16*(G/2) + 8*c' + (0..7) of step c = 2*kb + c'.
-    const int grp = lane >> 4, lg = lane & 15;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int r0 = 32 * (c >> 1) + 16 * (grp >> 1) + 8 * (c & 1) + (lg >> 2);
+      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kStride + vrow;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const int c0 = 32 * db + 16 * (grp & 1) + 4 * (lg & 3);
-        const s16x4 lo = lds_read_tr16(&sm.v[r0 * kStride + c0]);
-        const s16x4 hi = lds_read_tr16(&sm.v[(r0 + 4) * kStride + c0]);
+        const s16x4 lo = lds_read_tr16(&sm.v[r0 + 32 * db]);
+        const s16x4 hi = lds_read_tr16(&sm.v[r0 + 4 * kStride + 32 * db]);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pop[c], oacc[db]);
       }
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
         *reinterpret_cast<uint2*>(op + 32 * db + 8 * a + 4 * half) = w;
       }
     }
-    if (half == 0) p.lse_out[((int64_t)bb * p.hq + hh_q) * p.s + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (half == 0) p.lse_out[((int64_t)bb * p.hq + hh_q) * p.s + qi] = (m_use + __log2f(l_tot)) * kLn2;
   }
 }
 

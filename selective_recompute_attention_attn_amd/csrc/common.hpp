@@ -53,7 +53,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) s16x4*)(uintptr_t)p);
 }
 
-template <typename T>
-__device__ __forceinline__ T ldg(const T* p) { return __builtin_nontemporal_load(p); }
+// Row stride (bf16 elements) of a D-wide tile in LDS: D/2 + pad dwords with the
+// total = 20 (mod 32).  Measured on gfx950, that stride keeps both 16-byte
+// row reads across 32 rows and ds_read_b64_tr_b16 4-row groups free of bank
+// conflicts (strides = 24 (mod 32) double the row-read cost).
+template <int D>
+struct TileStride {
+  static constexpr int kPadDwords = ((20 - (D / 2) % 32) + 32) % 32;
+  static constexpr int kValue = D + 2 * kPadDwords;
+};
 
 }  // namespace srat

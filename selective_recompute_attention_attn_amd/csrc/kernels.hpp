@@ -67,9 +67,8 @@ struct AttnParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;       // [b, s, hq, d] fp32 workspace
-  float* dk_part;      // grouped-query attention: [b, s, hq, d] fp32 per-q-head partials
-  float* dv_part;
+  float* dk_acc;       // grouped-query attention: [b, s, hq, d] fp32 per-q-head dK partials
+  float* dv_acc;       // ... and dV partials
   float* delta;        // [b, hq, s] rowsum(dO * O)
   int64_t sq_b, sq_s, sq_h;
   int64_t sk_b, sk_s, sk_h;

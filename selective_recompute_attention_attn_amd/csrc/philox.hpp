@@ -25,6 +25,18 @@ struct Philox4 {
   uint32_t w[4];
 };
 
+// a ^ b ^ k with k uniform across the wavefront: one v_bitop3_b32 (truth
+// table 0x96) on gfx950 instead of two xors.
+SRAT_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+#if defined(__HIP_DEVICE_COMPILE__) && defined(__gfx950__)
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+#else
+  return a ^ b ^ k;
+#endif
+}
+
 // One call: counter (c0..c3), key (k0, k1).  Each round multiplies counter
 // words 0 and 2 by the round constants (32x32 -> 64 bits), xors the high
 // halves into the other two words and the key, keeps the low halves, and
@@ -39,8 +51,8 @@ SRAT_HD Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3
   for (int r = 0; r < 10; ++r) {
     const uint64_t pa = (uint64_t)c0 * kMulA;
     const uint64_t pb = (uint64_t)c2 * kMulB;
-    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
     c1 = (uint32_t)pb;
     c3 = (uint32_t)pa;
     c0 = n0;

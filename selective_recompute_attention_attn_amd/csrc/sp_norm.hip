@@ -226,25 +226,37 @@ __global__ __launch_bounds__(BLOCK) void sp_norm_bwd_kernel(NormBwdParams p) {
   }
 }
 
-// dgamma[c] = sum over blocks of partial[blk][0][c]; dbeta likewise.
+// dgamma[c] = sum over blocks of partial[blk][0][c]; dbeta likewise
+// (blockIdx.y = 0 / 1).  A workgroup owns 64 columns: 16 threads x float4
+// across them, 16 thread rows striding over the partial blocks, then a
+// reduction of the 16 row sums through LDS.
 __global__ __launch_bounds__(256) void sp_norm_colsum_kernel(const float* partial, int nblk, int hdim,
                                                               float* dgamma, float* dbeta) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= hdim) return;
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-  int k = 0;
-  for (; k + 1 < nblk; k += 2) {
-    a0 += partial[(int64_t)k * 2 * hdim + c];
-    b0 += partial[(int64_t)k * 2 * hdim + hdim + c];
-    a1 += partial[(int64_t)(k + 1) * 2 * hdim + c];
-    b1 += partial[(int64_t)(k + 1) * 2 * hdim + hdim + c];
+  __shared__ float4 red[16][16];
+  const int which = blockIdx.y;
+  float* out = which ? dbeta : dgamma;
+  if (out == nullptr) return;                       // RMSNorm has no dbeta
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int c = blockIdx.x * 64 + 4 * tx;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < hdim) {
+    const float* src = partial + (int64_t)which * hdim + c;
+    for (int k = ty; k < nblk; k += 16) {
+      const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)k * 2 * hdim);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
   }
-  if (k < nblk) {
-    a0 += partial[(int64_t)k * 2 * hdim + c];
-    b0 += partial[(int64_t)k * 2 * hdim + hdim + c];
+  red[ty][tx] = acc;
+  __syncthreads();
+  if (ty == 0 && c < hdim) {
+    float4 t = red[0][tx];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      const float4 v = red[r][tx];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + c) = t;
   }
-  dgamma[c] = a0 + a1;
-  if (dbeta) dbeta[c] = b0 + b1;
 }
 
 __global__ void hidden_mask_kernel(NormFwdParams p, uint8_t* mask) {
@@ -352,8 +364,8 @@ hipError_t launch_norm_bwd(const NormBwdParams& p0, bool bf16, bool rms, hipStre
   NormBwdParams p = p0;
   if (p.rows == 0) {
     // no rows: dgamma / dbeta are empty sums, written as zeros by the column sum
-    sp_norm_colsum_kernel<<<(p.hdim + 255) / 256, 256, 0, st>>>(p.partial, 0, p.hdim, p.dgamma,
-                                                                rms ? nullptr : p.dbeta);
+    sp_norm_colsum_kernel<<<dim3((p.hdim + 63) / 64, 2), 256, 0, st>>>(p.partial, 0, p.hdim, p.dgamma,
+                                                                        rms ? nullptr : p.dbeta);
     return hipGetLastError();
   }
   p.rows_per_block = (int32_t)rows_per_block(p.rows, p.hdim);
@@ -364,8 +376,8 @@ hipError_t launch_norm_bwd(const NormBwdParams& p0, bool bf16, bool rms, hipStre
     if (e != hipSuccess) return e;
   }
   TraceScope ts("sp_norm_colsum", st);
-  sp_norm_colsum_kernel<<<(p.hdim + 255) / 256, 256, 0, st>>>(p.partial, nblk, p.hdim, p.dgamma,
-                                                              rms ? nullptr : p.dbeta);
+  sp_norm_colsum_kernel<<<dim3((p.hdim + 63) / 64, 2), 256, 0, st>>>(p.partial, nblk, p.hdim, p.dgamma,
+                                                                      rms ? nullptr : p.dbeta);
   return hipGetLastError();
 }
 

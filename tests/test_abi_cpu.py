@@ -59,7 +59,8 @@ def _err(L, rc):
     (dict(d=48), -2), (dict(d=256), -2), (dict(p_drop=1.0), -1), (dict(p_drop=-0.1), -1),
     (dict(hq=4, hkv=3), -1), (dict(dtype=7), -1), (dict(causal=2), -1), (dict(s=-1), -1),
     (dict(q_stride=(256 * 4 * 64, 4 * 64, 60)), -1), (dict(k_stride=(0, 3, 64)), -1),
-    (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1)])
+    (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1), (dict(scale=0.0), -1),
+    (dict(scale=-0.1), -1)])
 def test_attention_validation_before_any_hip_call(L, kw, code):
     d = _desc(**kw)
     n = ctypes.c_size_t(0)

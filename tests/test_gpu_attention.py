@@ -153,9 +153,12 @@ def test_forward_is_deterministic_and_bwd_close():
     x = gen.attn_inputs(a)
     r1 = run_gpu(a, x, device)
     r2 = run_gpu(a, x, device)
-    for n in ("o", "lse", "dk", "dv"):
+    for n in ("o", "lse"):
         np.testing.assert_array_equal(r1[n], r2[n])
-    assert_close("dq rerun", r2["dq"], r1["dq"], 1e-2)   # fp32 atomics: order may differ
+    # dQ, dK, dV are summed with fp32 atomics: the order, and so the last
+    # rounding, may differ between runs
+    for n in ("dq", "dk", "dv"):
+        assert_close(f"{n} rerun", r2[n], r1[n], 1e-2)
 
 
 def test_head_offset_split_invariance():
@@ -170,8 +173,8 @@ def test_head_offset_split_invariance():
         part = run_gpu(a.with_(hq=2, hkv=2, head_offset=lo), sub, device)
         np.testing.assert_array_equal(part["o"], full["o"][:, :, lo:lo + 2])
         np.testing.assert_array_equal(part["lse"], full["lse"][:, lo:lo + 2])
-        np.testing.assert_array_equal(part["dk"], full["dk"][:, :, lo:lo + 2])
-        np.testing.assert_array_equal(part["dv"], full["dv"][:, :, lo:lo + 2])
+        for n in ("dq", "dk", "dv"):        # atomics: same values up to summation order
+            assert_close(n, part[n], full[n][:, :, lo:lo + 2], 1e-2)
 
 
 def test_no_s_by_s_allocation():
