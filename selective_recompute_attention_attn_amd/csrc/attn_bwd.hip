@@ -44,6 +44,9 @@ namespace {
 constexpr int kBNk = 128;      // keys per dkdv workgroup
 
 __device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+// Inverse of perm32: the MFMA slot of key k of a 32-key block (LDS K / V
+// tiles of the dq kernel are stored in slot order).
+__device__ __forceinline__ int slot32(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
 
 // ds_read_b64_tr_b16 pair -> 32x32x16 MFMA operand "lane (i = l%32, h = l/32)
 // holds column c_base + i, rows r_base + 8h .. +7" of a row-major tile; this is
@@ -75,7 +78,7 @@ __device__ __forceinline__ bool keep16(const Philox4 (&rnd)[2], int r, uint32_t 
 constexpr int kWaveTile = 32 * 32;
 
 template <int D, int QH>
-struct DkdvSmem {
+struct alignas(16) DkdvSmem {
   static constexpr int kS = TileStride<D>::kValue;   // Q / dO tile row stride (bf16)
   static constexpr int kRows = 32 * QH;              // queries per tile
   union {
@@ -305,7 +308,7 @@ constexpr int kQM = 128;       // queries per dq workgroup
 constexpr int kQN = 64;        // keys per K/V tile
 
 template <int D>
-struct DqSmem {
+struct alignas(16) DqSmem {
   static constexpr int kStride = TileStride<D>::kValue;
   bf16 k[kQN * kStride];
   bf16 v[kQN * kStride];
@@ -385,16 +388,19 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     for (int it = 0; it < kLoads; ++it) {
       const int x = tid + 256 * it;
       const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.k[r * kStride + 8 * c8]) = kpre[it];
-      *reinterpret_cast<uint4*>(&sm.v[r * kStride + 8 * c8]) = vpre[it];
+      const int row = ((r & ~31) | slot32(r & 31)) * kStride + 8 * c8;   // slot order
+      *reinterpret_cast<uint4*>(&sm.k[row]) = kpre[it];
+      *reinterpret_cast<uint4*>(&sm.v[row]) = vpre[it];
     }
   };
 
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
   const uint32_t thr_hi = p.thresh << 16;
-  const int krow = perm32(col) * kStride + 8 * half;
+  const int krow = col * kStride + 8 * half;    // K, V tile rows are in slot order
+  // K^T operand of step c (keys 32*(c/2) + 16*h + 8*(c%2) + e of lane half h):
+  // in slot order those are rows 16*(c%2) + 4*h + (0..3) and the same + 8
   const int grp = lane >> 4, lg = lane & 15;
-  const int ktr = (16 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
+  const int ktr = (4 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
 
   prefetch(0);
   for (int kt = 0; kt < nkt; ++kt) {
@@ -445,11 +451,11 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     // dQ^T += K^T dS^T; K^T operand through LDS transpose reads
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kStride + ktr;
+      const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kStride + ktr;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const s16x4 lo = lds_read_tr16(&sm.k[r0 + 32 * db]);
-        const s16x4 hi = lds_read_tr16(&sm.k[r0 + 4 * kStride + 32 * db]);
+        const s16x4 hi = lds_read_tr16(&sm.k[r0 + 8 * kStride + 32 * db]);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         qacc[db] = mfma32(a, dsop[c], qacc[db]);
       }

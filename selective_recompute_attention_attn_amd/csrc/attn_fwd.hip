@@ -41,7 +41,7 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr float kMaxSlack = 8.0f;
 
 template <int D>
-struct FwdSmem {
+struct alignas(16) FwdSmem {
   static constexpr int kStride = TileStride<D>::kValue;
   bf16 k[kBN * kStride];
   bf16 v[kBN * kStride];
@@ -51,6 +51,9 @@ struct FwdSmem {
 // 8a + 4hh + jj hold keys 16hh + 4a + jj, so output register r of lane half hh
 // is key 16hh + r.
 __device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+// Inverse of perm32: the MFMA slot of key k of a 32-key block.  K rows are
+// stored in LDS in slot order, so the A-operand reads are consecutive rows.
+__device__ __forceinline__ int slot32(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
 
 // Causal q-tile order: the first half of the grid runs the longest tiles
 // first, the second half the shortest first, so two workgroups that share a
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
     for (int it = 0; it < kLoads; ++it) {
       const int x = tid + kThreads * it;
       const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.k[r * kStride + 8 * c8]) = kpre[it];
+      *reinterpret_cast<uint4*>(&sm.k[((r & ~31) | slot32(r & 31)) * kStride + 8 * c8]) = kpre[it];
       *reinterpret_cast<uint4*>(&sm.v[r * kStride + 8 * c8]) = vpre[it];
     }
   };
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const uint32_t thr_hi = p.thresh << 16;
   const float c2 = p.scale_log2;
   // LDS element offsets that do not change across tiles
-  const int krow = perm32(col) * kStride + 8 * half;
+  const int krow = col * kStride + 8 * half;   // K tile rows are in slot order
   const int grp = lane >> 4, lg = lane & 15;
   const int vrow = (16 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
 
