@@ -18,7 +18,6 @@ cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,6 +30,8 @@ METRIC = "attn-core fwd+bwd TFLOP/s & % bf16 MFMA peak; SP LayerNorm GB/s (1 GPU
 PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_HBM_GBPS = 8000.0
 N_SETS = 4                      # rotated input/output sets (> 2x the 256 MB last-level cache)
+COPY_CALIBRATION_BYTES = 1 << 29  # 512 MiB read + 512 MiB written per calibration copy
+COPY_CALIBRATION_REPS = 3
 
 
 def attn_flops(a, fwd=True, bwd=True):
@@ -53,25 +54,6 @@ def norm_bytes(n, fwd=True):
     return elems * tensors * e + stats + 2 * vecs
 
 
-def src_hash(*files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-_BWD_SRC = ["selective_recompute_attention_attn_amd/csrc/attn_bwd.hip",
-            "selective_recompute_attention_attn_amd/csrc/philox.hpp",
-            "selective_recompute_attention_attn_amd/csrc/common.hpp"]
-KERNEL_SOURCES = {
-    "attn_bwd_dkdv": _BWD_SRC,
-    "attn_bwd_dq": _BWD_SRC,
-    "attn_fwd_bf16": ["selective_recompute_attention_attn_amd/csrc/attn_fwd.hip",
-                      "selective_recompute_attention_attn_amd/csrc/philox.hpp",
-                      "selective_recompute_attention_attn_amd/csrc/common.hpp"],
-}
-
 # Algorithmic FLOPs per score element and head-dim unit of each attention
 # kernel: forward QK^T + PV = 4; backward 10 = QK^T recompute, dP, dV, dK (the
 # dK/dV kernel, 8) + dQ (the dQ kernel, 2; the QK^T and dO V^T it re-does to
@@ -82,12 +64,13 @@ KERNEL_FLOP_UNITS = {"attn_fwd_bf16": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel source changed since it was taken."""
+    from selective_recompute_attention_attn_amd import profiling
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+    if not os.path.exists(path) or kernel not in profiling.KERNEL_SOURCES:
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != src_hash(*KERNEL_SOURCES[kernel]):
+    if rec.get("source_hash") != profiling.src_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -148,6 +131,9 @@ def main():
     ap.add_argument("--workload", default="gpt22b-t8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="time without per-launch trace events")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="before warmup, run COPY_CALIBRATION_REPS plain device copies of "
+                         "COPY_CALIBRATION_BYTES (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -216,6 +202,13 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    if args.calibrate_copy:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_CALIBRATION_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
