@@ -182,7 +182,8 @@ def main():
     ws_attn = torch.empty(ops.attn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     ndesc = ops.norm_desc(sets[0]["resid"], norm=n.norm, eps=n.eps, p_drop=n.p_drop, seed=n.seed, site=n.site,
                           seq_offset=0)
-    ws_norm = torch.empty(max(ops.sp_norm_bwd_workspace_bytes(ndesc), 1), dtype=torch.uint8, device=dev)
+    need = ops.sp_norm_bwd_workspace_bytes(ndesc)
+    ws_norm = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     akw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed)
     nkw = dict(norm=n.norm, p_drop=n.p_drop, seed=n.seed, site=n.site)
 

@@ -153,7 +153,10 @@ int srat_sp_norm_fwd(const srat_norm_desc* desc, const void* resid, const void* 
                      const float* gamma, const float* beta, void* h_out, void* u_out,
                      float* mean, float* rstd, void* stream);
 
-/* Workspace bytes srat_sp_norm_bwd needs (per-block dgamma/dbeta partials). */
+/* Workspace bytes srat_sp_norm_bwd needs.  Currently 0 for every shape:
+ * dgamma / dbeta are summed over all rows by dedicated workgroups of the same
+ * launch, without scratch memory.  Kept so callers need not change should a
+ * later version use scratch. */
 int srat_sp_norm_bwd_workspace(const srat_norm_desc* desc, size_t* bytes);
 
 /*
@@ -163,7 +166,9 @@ int srat_sp_norm_bwd_workspace(const srat_norm_desc* desc, size_t* bytes);
  *   dy = dh * mask / (1 - p)
  *   dgamma = sum over rows of du * xhat;  dbeta = sum over rows of du
  * dy may equal dh only when p_drop == 0.  dbeta is ignored (may be NULL) for
- * RMSNorm.  ws: at least srat_sp_norm_bwd_workspace() bytes, 256-byte aligned.
+ * RMSNorm.  ws: at least srat_sp_norm_bwd_workspace() bytes, 256-byte aligned
+ * (may be NULL when that is 0).  dgamma / dbeta are reproducible bit for bit
+ * (fixed summation order).
  */
 int srat_sp_norm_bwd(const srat_norm_desc* desc, const void* du, const void* dres,
                      const void* h, const float* gamma, const float* mean, const float* rstd,

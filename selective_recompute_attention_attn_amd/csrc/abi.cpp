@@ -247,9 +247,7 @@ int srat_sp_norm_bwd_workspace(const srat_norm_desc* desc, size_t* bytes) {
   g_err.clear();
   if (int e = check_norm(desc)) return e;
   if (!bytes) return fail(SRAT_ERR_INVALID, "bytes is NULL");
-  const int64_t rows = desc->s_local * desc->b;
-  const int nblk = rows ? srat::norm_bwd_blocks(rows, (int)desc->h) : 0;
-  *bytes = align256((size_t)nblk * 2 * desc->h * sizeof(float));
+  *bytes = 0;   // dgamma / dbeta are summed without scratch memory
   return SRAT_OK;
 }
 
@@ -292,13 +290,16 @@ int srat_sp_norm_bwd(const srat_norm_desc* desc, const void* du, const void* dre
     for (const void* ptr : ptrs)
       if (!aligned(ptr, 16)) return fail(SRAT_ERR_INVALID, "tensor pointers must be 16-byte aligned");
     if (dy == dh && desc->p_drop != 0.f) return fail(SRAT_ERR_INVALID, "dy may alias dh only when p_drop == 0");
-    if (!ws || ws_bytes < need) return fail(SRAT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-    if (!aligned(ws, 256)) return fail(SRAT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (need && (!ws || ws_bytes < need))
+      return fail(SRAT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    if (need && !aligned(ws, 256)) return fail(SRAT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
+  (void)ws;
+  (void)ws_bytes;
   srat::NormBwdParams p{};
   norm_common(desc, p.rows, p.thresh, p.k0, p.k1, p.tag, p.inv_keep);
   p.du = du; p.dres = dres; p.h = h; p.gamma = gamma; p.mean = mean; p.rstd = rstd;
-  p.dh = dh; p.dy = dy; p.dgamma = dgamma; p.dbeta = dbeta; p.partial = static_cast<float*>(ws);
+  p.dh = dh; p.dy = dy; p.dgamma = dgamma; p.dbeta = dbeta;
   p.b = (int32_t)desc->b; p.hdim = (int32_t)desc->h; p.seq_offset = desc->seq_offset;
   hipError_t e = srat::launch_norm_bwd(p, desc->dtype == SRAT_BF16, rms, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sp_norm_bwd launch");

@@ -19,10 +19,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---- wavefront reductions (64 lanes) --------------------------------------
+// DPP lane exchange within rows of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 64 lanes, returned to every lane: quad_perm [1,0,3,2] and
+// [2,3,0,1], row_half_mirror, row_mirror reduce each row of 16 lanes, then
+// the four row sums are read from lanes 0, 16, 32, 48 (fixed order).
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  const int xi = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(xi, 0)) + __int_as_float(__builtin_amdgcn_readlane(xi, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(xi, 32)) + __int_as_float(__builtin_amdgcn_readlane(xi, 48)));
 }
 
 // ---- bf16 <-> fp32 ---------------------------------------------------------

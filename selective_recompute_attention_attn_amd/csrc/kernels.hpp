@@ -36,11 +36,10 @@ struct NormBwdParams {
   const float* rstd;
   void* dh;
   void* dy;            // == dh allowed when thresh == 0
-  float* partial;      // [blocks][2][hdim] dgamma / dbeta partial sums
   float* dgamma;
   float* dbeta;
   int64_t rows;
-  int32_t rows_per_block;
+  int32_t col_blocks;  // set by the launcher: workgroups summing dgamma / dbeta
   int32_t b;
   int32_t hdim;
   int64_t seq_offset;
@@ -48,8 +47,6 @@ struct NormBwdParams {
   uint32_t thresh, k0, k1, tag;
 };
 
-// Returns the number of blocks the backward row kernel will use (for the workspace).
-int norm_bwd_blocks(int64_t rows, int hdim);
 hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStream_t st);
 hipError_t launch_norm_bwd(const NormBwdParams& p, bool bf16, bool rms, hipStream_t st);
 hipError_t launch_hidden_mask(const NormFwdParams& p, uint8_t* mask, hipStream_t st);

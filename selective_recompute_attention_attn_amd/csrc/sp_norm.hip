@@ -11,6 +11,8 @@
 // row held in registers between the reduction and the output pass, the dropout
 // mask regenerated from Philox (one call per 8 columns, matching one 16-byte
 // bf16 vector).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
@@ -18,31 +20,41 @@
 namespace srat {
 namespace {
 
-// 8 consecutive elements <-> fp32 registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements <-> fp32 registers.  NT = non-temporal (streamed
+// once: no reuse expected from the caches).
+template <bool NT = false>
 __device__ __forceinline__ void load8(const bf16* p, float v[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  const u32x4 w = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
+                     : *reinterpret_cast<const u32x4*>(p);
+  v[0] = bf16_lo(w[0]); v[1] = bf16_hi(w[0]);
+  v[2] = bf16_lo(w[1]); v[3] = bf16_hi(w[1]);
+  v[4] = bf16_lo(w[2]); v[5] = bf16_hi(w[2]);
+  v[6] = bf16_lo(w[3]); v[7] = bf16_hi(w[3]);
 }
+template <bool NT = false>
 __device__ __forceinline__ void load8(const float* p, float v[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const u32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
+  const u32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v[e] = __uint_as_float(a[e]); v[4 + e] = __uint_as_float(b[e]); }
 }
-__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
-  uint4 w;
-  w.x = pack_bf16x2(v[0], v[1]);
-  w.y = pack_bf16x2(v[2], v[3]);
-  w.z = pack_bf16x2(v[4], v[5]);
-  w.w = pack_bf16x2(v[6], v[7]);
-  *reinterpret_cast<uint4*>(p) = w;
+__device__ __forceinline__ void store8_nt(bf16* p, const float v[8]) {
+  u32x4 w;
+  w[0] = pack_bf16x2(v[0], v[1]);
+  w[1] = pack_bf16x2(v[2], v[3]);
+  w[2] = pack_bf16x2(v[4], v[5]);
+  w[3] = pack_bf16x2(v[6], v[7]);
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
-__device__ __forceinline__ void store8(float* p, const float v[8]) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+__device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
+  u32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = __float_as_uint(v[e]); b[e] = __float_as_uint(v[4 + e]); }
+  __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(p) + 1);
 }
 
 // Sum of `n` values per thread over the block; every thread gets the totals.
@@ -69,31 +81,47 @@ __device__ __forceinline__ void block_sum(float (&x)[N], float* red) {
   }
 }
 
-template <typename T, int BLOCK, int NIT, bool RMS, bool DROP>
-__global__ __launch_bounds__(BLOCK) void sp_norm_fwd_kernel(NormFwdParams p) {
-  __shared__ float red[2 * (BLOCK / kWave)];
-  const int64_t row = blockIdx.x;
-  const int hdim = p.hdim;
-  const uint32_t bb = (uint32_t)(row % p.b);
-  const uint32_t sg = (uint32_t)(p.seq_offset + row / p.b);
-  const T* resid = static_cast<const T*>(p.resid) + row * hdim;
-  const T* y = static_cast<const T*>(p.y) + row * hdim;
-
-  float hv[NIT][8];
-  float acc[1] = {0.f};
+// Forward.  A workgroup owns rows blockIdx.x, blockIdx.x + gridDim.x, ...;
+// with PIPE the loads of its next row are issued before the current row is
+// reduced and written, so each CU keeps reading while it writes.  gamma / beta
+// stay in registers across the rows.  Every row is held in registers through
+// its two reductions (mean, then the variance of the held values), and h, u
+// are streamed out with non-temporal stores.
+template <typename T, int NIT, int BLOCK>
+__device__ __forceinline__ void fwd_load(const NormFwdParams& p, int64_t row, float (&x)[NIT][8],
+                                         float (&y)[NIT][8]) {
+  const T* resid = static_cast<const T*>(p.resid) + row * p.hdim;
+  const T* yy = static_cast<const T*>(p.y) + row * p.hdim;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;   // 8-column group
+    if (8 * c < p.hdim) {
+      load8<true>(resid + 8 * c, x[it]);
+      load8<true>(yy + 8 * c, y[it]);
+    }
+  }
+}
+
+// HOLD: gamma / beta come in registers (g, bt); otherwise they are loaded
+// here, next to their use (large rows, where registers are short).
+template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool HOLD>
+__device__ __forceinline__ void fwd_row(const NormFwdParams& p, int64_t row, float (&hv)[NIT][8],
+                                        const float (&yv)[NIT][8], const float (&g)[NIT][8],
+                                        const float (&bt)[NIT][8], float* red) {
+  const int hdim = p.hdim;
+  const uint32_t bb = (uint32_t)(row % p.b);
+  const uint32_t sg = (uint32_t)(p.seq_offset + row / p.b);
+  float acc[1] = {0.f};
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = threadIdx.x + it * BLOCK;
     if (8 * c < hdim) {
-      float r[8], yy[8];
-      load8(resid + 8 * c, r);
-      load8(y + 8 * c, yy);
       uint32_t keep = 0xFFu;
       if (DROP) keep = hidden_keep8(p.k0, p.k1, p.tag, sg, bb, (uint32_t)c, p.thresh);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float yd = ((keep >> e) & 1u) ? yy[e] * p.inv_keep : 0.f;
-        hv[it][e] = r[e] + (DROP ? yd : yy[e]);
+        const float yd = ((keep >> e) & 1u) ? yv[it][e] * p.inv_keep : 0.f;
+        hv[it][e] = hv[it][e] + (DROP ? yd : yv[it][e]);
         acc[0] += RMS ? hv[it][e] * hv[it][e] : hv[it][e];
       }
     } else {
@@ -128,14 +156,19 @@ __global__ __launch_bounds__(BLOCK) void sp_norm_fwd_kernel(NormFwdParams p) {
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;
     if (8 * c < hdim) {
-      float g[8], bt[8], u[8];
-      load8(p.gamma + 8 * c, g);
-      if (!RMS) load8(p.beta + 8 * c, bt);
+      float u[8], gl[8], bl[8];
+      if (!HOLD) {
+        load8(p.gamma + 8 * c, gl);
+        if (!RMS) load8(p.beta + 8 * c, bl);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        u[e] = RMS ? hv[it][e] * rs * g[e] : (hv[it][e] - mu) * rs * g[e] + bt[e];
-      store8(hout + 8 * c, hv[it]);
-      store8(uout + 8 * c, u);
+      for (int e = 0; e < 8; ++e) {
+        const float ge = HOLD ? g[it][e] : gl[e];
+        const float be = RMS ? 0.f : (HOLD ? bt[it][e] : bl[e]);
+        u[e] = RMS ? hv[it][e] * rs * ge : (hv[it][e] - mu) * rs * ge + be;
+      }
+      store8_nt(hout + 8 * c, hv[it]);
+      store8_nt(uout + 8 * c, u);
     }
   }
   if (threadIdx.x == 0) {
@@ -144,119 +177,230 @@ __global__ __launch_bounds__(BLOCK) void sp_norm_fwd_kernel(NormFwdParams p) {
   }
 }
 
-template <typename T, int BLOCK, int NIT, bool RMS, bool DROP>
-__global__ __launch_bounds__(BLOCK) void sp_norm_bwd_kernel(NormBwdParams p) {
+template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool PIPE>
+__global__ __launch_bounds__(BLOCK) void sp_norm_fwd_kernel(NormFwdParams p) {
+  constexpr bool kHold = NIT <= 3;
   __shared__ float red[2 * (BLOCK / kWave)];
-  const int hdim = p.hdim;
-  const float inv_n = 1.0f / (float)hdim;
-  const bool separate_dy = p.dy != p.dh;
-  float gam[NIT][8], adg[NIT][8], adb[NIT][8];
+  float g[NIT][8], bt[NIT][8];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;
-    if (8 * c < hdim) load8(p.gamma + 8 * c, gam[it]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) adg[it][e] = adb[it][e] = 0.f;
+    if (kHold && 8 * c < p.hdim) {
+      load8(p.gamma + 8 * c, g[it]);
+      if (!RMS) load8(p.beta + 8 * c, bt[it]);
+    }
   }
-  const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
-  const int64_t r1 = min(r0 + p.rows_per_block, p.rows);
-  for (int64_t row = r0; row < r1; ++row) {
-    const T* du = static_cast<const T*>(p.du) + row * hdim;
-    const T* dres = static_cast<const T*>(p.dres) + row * hdim;
-    const T* h = static_cast<const T*>(p.h) + row * hdim;
-    const float mu = RMS ? 0.f : p.mean[row];
-    const float rs = p.rstd[row];
-    float xh[NIT][8], g[NIT][8];
-    float sums[2] = {0.f, 0.f};
+  const int64_t stride = gridDim.x;
+  int64_t row = blockIdx.x;             // < rows: the grid never exceeds the row count
+  float xa[NIT][8], ya[NIT][8];
+  fwd_load<T, NIT, BLOCK>(p, row, xa, ya);
+  if (!PIPE) {
+    fwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, row, xa, ya, g, bt, red);
+    return;
+  }
+  float xb[NIT][8], yb[NIT][8];
+  while (true) {
+    const int64_t r1 = row + stride;
+    if (r1 < p.rows) fwd_load<T, NIT, BLOCK>(p, r1, xb, yb);
+    fwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, row, xa, ya, g, bt, red);
+    if (r1 >= p.rows) break;
+    const int64_t r2 = r1 + stride;
+    if (r2 < p.rows) fwd_load<T, NIT, BLOCK>(p, r2, xa, ya);
+    fwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, r1, xb, yb, g, bt, red);
+    if (r2 >= p.rows) break;
+    row = r2;
+  }
+}
+
+// Backward, one launch with two kinds of workgroup:
+//  * the first `col_blocks` workgroups each own a slab of 32 columns and sum
+//    dgamma = sum_rows du * xhat and dbeta = sum_rows du over ALL rows (rows
+//    split over BLOCK/4 thread groups, then a fixed-order reduction), so the
+//    sums need no partials in memory, no atomics, and are reproducible;
+//  * the other workgroups each own one row: all loads issued up front, the
+//    two row sums, then dh and dy streamed out.
+// Both read du and h (the column pass re-reads 4 bytes per element instead of
+// writing and reading per-block partials, which cost more when rows are few).
+constexpr int kColSlab = 32;
+
+// slab handled by column workgroup `bid`: consecutive slabs (which share
+// 128-byte lines of every row) go to the same XCD, which receives every
+// eighth workgroup of the launch
+__device__ __forceinline__ int xcd_slab(int bid, int col_blocks) {
+  const int per = col_blocks / 8;
+  return (bid % 8) * per + bid / 8;
+}
+
+template <typename T, int BLOCK, bool RMS>
+__device__ __forceinline__ void colsum_job(const NormBwdParams& p, int slab, float* red) {
+  constexpr int kRG = BLOCK / 4;
+  constexpr int kU = BLOCK >= 1024 ? 4 : 8;   // rows in flight per thread (register budget)
+  const int v = threadIdx.x & 3, rg = threadIdx.x >> 2;
+  const int hdim = p.hdim;
+  const int c = kColSlab * slab + 8 * v;
+  float ag[8], ab[8];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int c = threadIdx.x + it * BLOCK;
-      if (8 * c < hdim) {
-        float hh[8], d[8];
-        load8(h + 8 * c, hh);
-        load8(du + 8 * c, d);
+  for (int e = 0; e < 8; ++e) ag[e] = ab[e] = 0.f;
+  if (c < hdim) {
+    const T* du = static_cast<const T*>(p.du) + c;
+    const T* h = static_cast<const T*>(p.h) + c;
+    int64_t r = rg;
+    for (; r + (int64_t)(kU - 1) * kRG < p.rows; r += (int64_t)kU * kRG) {
+      float d[kU][8], x[kU][8], mu[kU], rs[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t rr = r + (int64_t)u * kRG;
+        load8(du + rr * hdim, d[u]);
+        load8(h + rr * hdim, x[u]);
+        mu[u] = RMS ? 0.f : p.mean[rr];
+        rs[u] = p.rstd[rr];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xh[it][e] = (hh[e] - mu) * rs;
-          g[it][e] = d[e] * gam[it][e];
-          sums[0] += g[it][e];
-          sums[1] += g[it][e] * xh[it][e];
-          adg[it][e] += d[e] * xh[it][e];
-          adb[it][e] += d[e];
+          ag[e] += d[u][e] * ((x[u][e] - mu[u]) * rs[u]);
+          ab[e] += d[u][e];
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xh[it][e] = g[it][e] = 0.f;
-      }
     }
-    block_sum<BLOCK>(sums, red);
-    const float mg = RMS ? 0.f : sums[0] * inv_n;
-    const float mgx = sums[1] * inv_n;
-    const uint32_t bb = (uint32_t)(row % p.b);
-    const uint32_t sg = (uint32_t)(p.seq_offset + row / p.b);
-    T* dh = static_cast<T*>(p.dh) + row * hdim;
-    T* dy = static_cast<T*>(p.dy) + row * hdim;
+    for (; r < p.rows; r += kRG) {
+      float d[8], x[8];
+      load8(du + r * hdim, d);
+      load8(h + r * hdim, x);
+      const float mu = RMS ? 0.f : p.mean[r], rs = p.rstd[r];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int c = threadIdx.x + it * BLOCK;
-      if (8 * c < hdim) {
-        float dr[8], o[8], oy[8];
-        load8(dres + 8 * c, dr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = rs * (g[it][e] - mg - xh[it][e] * mgx) + dr[e];
-        store8(dh + 8 * c, o);
-        if (separate_dy) {
-          uint32_t keep = 0xFFu;
-          if (DROP) keep = hidden_keep8(p.k0, p.k1, p.tag, sg, bb, (uint32_t)c, p.thresh);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) oy[e] = ((keep >> e) & 1u) ? o[e] * p.inv_keep : 0.f;
-          store8(dy + 8 * c, oy);
-        }
+      for (int e = 0; e < 8; ++e) {
+        ag[e] += d[e] * ((x[e] - mu) * rs);
+        ab[e] += d[e];
       }
     }
   }
-  float* part = p.partial + (int64_t)blockIdx.x * 2 * hdim;
+  // lanes with equal (lane & 3) hold the same columns: sum over lane bits 2..5
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = threadIdx.x + it * BLOCK;
-    if (8 * c < hdim) {
-      store8(part + 8 * c, adg[it]);
-      store8(part + hdim + 8 * c, adb[it]);
+  for (int off = 4; off < kWave; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ag[e] += __shfl_xor(ag[e], off, kWave);
+      ab[e] += __shfl_xor(ab[e], off, kWave);
+    }
+  constexpr int kWaves = BLOCK / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  if (lane < 4) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red[(wv * 4 + lane) * 16 + e] = ag[e];
+      red[(wv * 4 + lane) * 16 + 8 + e] = ab[e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int vv = threadIdx.x >> 4, k = threadIdx.x & 15;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[(w * 4 + vv) * 16 + k];
+    const int col = kColSlab * slab + 8 * vv + (k & 7);
+    if (col < hdim) {
+      if (k < 8) p.dgamma[col] = t;
+      else if (!RMS) p.dbeta[col] = t;
     }
   }
 }
 
-// dgamma[c] = sum over blocks of partial[blk][0][c]; dbeta likewise
-// (blockIdx.y = 0 / 1).  A workgroup owns 64 columns: 16 threads x float4
-// across them, 16 thread rows striding over the partial blocks, then a
-// reduction of the 16 row sums through LDS.
-__global__ __launch_bounds__(256) void sp_norm_colsum_kernel(const float* partial, int nblk, int hdim,
-                                                              float* dgamma, float* dbeta) {
-  __shared__ float4 red[16][16];
-  const int which = blockIdx.y;
-  float* out = which ? dbeta : dgamma;
-  if (out == nullptr) return;                       // RMSNorm has no dbeta
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int c = blockIdx.x * 64 + 4 * tx;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < hdim) {
-    const float* src = partial + (int64_t)which * hdim + c;
-    for (int k = ty; k < nblk; k += 16) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)k * 2 * hdim);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-  }
-  red[ty][tx] = acc;
-  __syncthreads();
-  if (ty == 0 && c < hdim) {
-    float4 t = red[0][tx];
+template <typename T, int NIT, int BLOCK>
+__device__ __forceinline__ void bwd_load(const NormBwdParams& p, int64_t row, float (&x)[NIT][8],
+                                         float (&d)[NIT][8], float (&r)[NIT][8]) {
+  const T* h = static_cast<const T*>(p.h) + row * p.hdim;
+  const T* du = static_cast<const T*>(p.du) + row * p.hdim;
+  const T* dres = static_cast<const T*>(p.dres) + row * p.hdim;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      const float4 v = red[r][tx];
-      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+  for (int it = 0; it < NIT; ++it) {
+    const int c = threadIdx.x + it * BLOCK;
+    if (8 * c < p.hdim) {
+      load8(h + 8 * c, x[it]);
+      load8(du + 8 * c, d[it]);
+      load8<true>(dres + 8 * c, r[it]);
     }
-    *reinterpret_cast<float4*>(out + c) = t;
   }
+}
+
+template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool HOLD>
+__device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, float (&xh)[NIT][8],
+                                        float (&g)[NIT][8], const float (&dr)[NIT][8],
+                                        const float (&gam)[NIT][8], float* red) {
+  const int hdim = p.hdim;
+  const float inv_n = 1.0f / (float)hdim;
+  const float mu = RMS ? 0.f : p.mean[row];
+  const float rs = p.rstd[row];
+  float sums[2] = {0.f, 0.f};
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = threadIdx.x + it * BLOCK;
+    if (8 * c < hdim) {
+      float gl[8];
+      if (!HOLD) load8(p.gamma + 8 * c, gl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xh[it][e] = (xh[it][e] - mu) * rs;
+        g[it][e] = g[it][e] * (HOLD ? gam[it][e] : gl[e]);
+        sums[0] += g[it][e];
+        sums[1] += g[it][e] * xh[it][e];
+      }
+    }
+  }
+  block_sum<BLOCK>(sums, red);
+  const float mg = RMS ? 0.f : sums[0] * inv_n;
+  const float mgx = sums[1] * inv_n;
+  const bool separate_dy = p.dy != p.dh;
+  const uint32_t bb = (uint32_t)(row % p.b);
+  const uint32_t sg = (uint32_t)(p.seq_offset + row / p.b);
+  T* dh = static_cast<T*>(p.dh) + row * hdim;
+  T* dy = static_cast<T*>(p.dy) + row * hdim;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = threadIdx.x + it * BLOCK;
+    if (8 * c < hdim) {
+      float o[8], oy[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rs * (g[it][e] - mg - xh[it][e] * mgx) + dr[it][e];
+      store8_nt(dh + 8 * c, o);
+      if (separate_dy) {
+        uint32_t keep = 0xFFu;
+        if (DROP) keep = hidden_keep8(p.k0, p.k1, p.tag, sg, bb, (uint32_t)c, p.thresh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oy[e] = ((keep >> e) & 1u) ? o[e] * p.inv_keep : 0.f;
+        store8_nt(dy + 8 * c, oy);
+      }
+    }
+  }
+}
+
+// Row workgroups: one row each, every load issued up front, gamma held in
+// registers.  (Walking two rows with prefetch, as the forward does, measured
+// slower here: the column workgroups already keep the memory busy.)
+template <typename T, int BLOCK, int NIT, bool RMS, bool DROP>
+__device__ __forceinline__ void bwd_rows(const NormBwdParams& p, int64_t row, float* red) {
+  constexpr bool kHold = NIT <= 3;
+  float gam[NIT][8];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = threadIdx.x + it * BLOCK;
+    if (kHold && 8 * c < p.hdim) load8(p.gamma + 8 * c, gam[it]);
+  }
+  float xa[NIT][8], da[NIT][8], ra[NIT][8];
+  bwd_load<T, NIT, BLOCK>(p, row, xa, da, ra);
+  bwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, row, xa, da, ra, gam, red);
+}
+
+template <typename T, int BLOCK, int NIT, bool RMS, bool DROP>
+__global__ __launch_bounds__(BLOCK) void sp_norm_bwd_kernel(NormBwdParams p) {
+  __shared__ float red[(BLOCK / kWave) * 4 * 16];
+  const int bid = blockIdx.x;
+  if (bid < p.col_blocks) {
+    const int slab = xcd_slab(bid, p.col_blocks);
+    if (kColSlab * slab < p.hdim) colsum_job<T, BLOCK, RMS>(p, slab, red);
+    return;
+  }
+  bwd_rows<T, BLOCK, NIT, RMS, DROP>(p, bid - p.col_blocks, red);
 }
 
 __global__ void hidden_mask_kernel(NormFwdParams p, uint8_t* mask) {
@@ -269,36 +413,48 @@ __global__ void hidden_mask_kernel(NormFwdParams p, uint8_t* mask) {
   }
 }
 
-// Block size so that each thread holds at most 4 groups of 8 columns.
+// Block size so that each thread holds at most 3 groups of 8 columns (4 only
+// in 1024-thread blocks, for rows above 24576 elements).
 int pick_block(int hdim) {
   const int groups = (hdim + 7) / 8;
   int block = 64;
-  while (block < 1024 && (groups + block - 1) / block > 4) block *= 2;
+  while (block < 1024 && (groups + block - 1) / block > 3) block *= 2;
   return block;
+}
+
+// Forward workgroups: up to 512, each walking rows with one row of prefetch
+// when it has more than one (PIPE; blocks of up to 512 threads keep two rows
+// in registers without spilling).  1024-thread blocks take one row each.
+constexpr int kMaxRowBlocks = 512;
+int64_t row_blocks(int64_t rows, int block) {
+  return block <= 512 ? std::min<int64_t>(rows, kMaxRowBlocks) : rows;
 }
 
 template <typename T, int BLOCK, bool RMS, bool DROP>
 hipError_t fwd_nit(const NormFwdParams& p, hipStream_t st) {
   const int nit = ((p.hdim + 7) / 8 + BLOCK - 1) / BLOCK;
-  dim3 grid((unsigned)p.rows);
+  constexpr bool kPipe = BLOCK <= 512;
+  dim3 grid((unsigned)row_blocks(p.rows, BLOCK));
+  constexpr int kMaxNit = BLOCK == 1024 ? 4 : 3;
   switch (nit) {
-    case 1: sp_norm_fwd_kernel<T, BLOCK, 1, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
-    case 2: sp_norm_fwd_kernel<T, BLOCK, 2, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
-    case 3: sp_norm_fwd_kernel<T, BLOCK, 3, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
-    default: sp_norm_fwd_kernel<T, BLOCK, 4, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
+    case 1: sp_norm_fwd_kernel<T, BLOCK, 1, RMS, DROP, kPipe><<<grid, BLOCK, 0, st>>>(p); break;
+    case 2: sp_norm_fwd_kernel<T, BLOCK, 2, RMS, DROP, kPipe><<<grid, BLOCK, 0, st>>>(p); break;
+    case 3: sp_norm_fwd_kernel<T, BLOCK, 3, RMS, DROP, kPipe><<<grid, BLOCK, 0, st>>>(p); break;
+    default: sp_norm_fwd_kernel<T, BLOCK, kMaxNit, RMS, DROP, kPipe><<<grid, BLOCK, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
 template <typename T, int BLOCK, bool RMS, bool DROP>
-hipError_t bwd_nit(const NormBwdParams& p, int nblk, hipStream_t st) {
+hipError_t bwd_nit(NormBwdParams p, hipStream_t st) {
   const int nit = ((p.hdim + 7) / 8 + BLOCK - 1) / BLOCK;
-  dim3 grid((unsigned)nblk);
+  dim3 grid((unsigned)(p.col_blocks + p.rows));
+  constexpr int kMaxNit = BLOCK == 1024 ? 4 : 3;
   switch (nit) {
     case 1: sp_norm_bwd_kernel<T, BLOCK, 1, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
     case 2: sp_norm_bwd_kernel<T, BLOCK, 2, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
     case 3: sp_norm_bwd_kernel<T, BLOCK, 3, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
-    default: sp_norm_bwd_kernel<T, BLOCK, 4, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
+    default: sp_norm_bwd_kernel<T, BLOCK, kMaxNit, RMS, DROP><<<grid, BLOCK, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -315,13 +471,13 @@ hipError_t fwd_block(const NormFwdParams& p, hipStream_t st) {
 }
 
 template <typename T, bool RMS, bool DROP>
-hipError_t bwd_block(const NormBwdParams& p, int nblk, hipStream_t st) {
+hipError_t bwd_block(const NormBwdParams& p, hipStream_t st) {
   switch (pick_block(p.hdim)) {
-    case 64: return bwd_nit<T, 64, RMS, DROP>(p, nblk, st);
-    case 128: return bwd_nit<T, 128, RMS, DROP>(p, nblk, st);
-    case 256: return bwd_nit<T, 256, RMS, DROP>(p, nblk, st);
-    case 512: return bwd_nit<T, 512, RMS, DROP>(p, nblk, st);
-    default: return bwd_nit<T, 1024, RMS, DROP>(p, nblk, st);
+    case 64: return bwd_nit<T, 64, RMS, DROP>(p, st);
+    case 128: return bwd_nit<T, 128, RMS, DROP>(p, st);
+    case 256: return bwd_nit<T, 256, RMS, DROP>(p, st);
+    case 512: return bwd_nit<T, 512, RMS, DROP>(p, st);
+    default: return bwd_nit<T, 1024, RMS, DROP>(p, st);
   }
 }
 
@@ -333,25 +489,17 @@ hipError_t fwd_dispatch(const NormFwdParams& p, bool rms, hipStream_t st) {
 }
 
 template <typename T>
-hipError_t bwd_dispatch(const NormBwdParams& p, int nblk, bool rms, hipStream_t st) {
+hipError_t bwd_dispatch(const NormBwdParams& p, bool rms, hipStream_t st) {
   const bool drop = p.thresh != 0;
-  if (rms) return drop ? bwd_block<T, true, true>(p, nblk, st) : bwd_block<T, true, false>(p, nblk, st);
-  return drop ? bwd_block<T, false, true>(p, nblk, st) : bwd_block<T, false, false>(p, nblk, st);
+  if (rms) return drop ? bwd_block<T, true, true>(p, st) : bwd_block<T, true, false>(p, st);
+  return drop ? bwd_block<T, false, true>(p, st) : bwd_block<T, false, false>(p, st);
 }
 
 }  // namespace
 
-int norm_bwd_blocks(int64_t rows, int hdim) {
-  (void)hdim;
-  // about 256 row blocks: enough to cover the 256 CUs, few enough that the
-  // dgamma/dbeta partials stay small next to the row traffic
-  const int64_t rpb = rows >= 512 ? rows / 256 : 1;
-  return (int)((rows + rpb - 1) / rpb);
-}
-
-static int64_t rows_per_block(int64_t rows, int hdim) {
-  const int nblk = norm_bwd_blocks(rows, hdim);
-  return (rows + nblk - 1) / nblk;
+int norm_bwd_col_blocks(int hdim) {
+  const int nslab = (hdim + kColSlab - 1) / kColSlab;
+  return 8 * ((nslab + 7) / 8);
 }
 
 hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStream_t st) {
@@ -362,23 +510,10 @@ hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStrea
 
 hipError_t launch_norm_bwd(const NormBwdParams& p0, bool bf16, bool rms, hipStream_t st) {
   NormBwdParams p = p0;
-  if (p.rows == 0) {
-    // no rows: dgamma / dbeta are empty sums, written as zeros by the column sum
-    sp_norm_colsum_kernel<<<dim3((p.hdim + 63) / 64, 2), 256, 0, st>>>(p.partial, 0, p.hdim, p.dgamma,
-                                                                        rms ? nullptr : p.dbeta);
-    return hipGetLastError();
-  }
-  p.rows_per_block = (int32_t)rows_per_block(p.rows, p.hdim);
-  const int nblk = (int)((p.rows + p.rows_per_block - 1) / p.rows_per_block);
-  {
-    TraceScope ts("sp_norm_bwd", st);
-    hipError_t e = bf16 ? bwd_dispatch<srat::bf16>(p, nblk, rms, st) : bwd_dispatch<float>(p, nblk, rms, st);
-    if (e != hipSuccess) return e;
-  }
-  TraceScope ts("sp_norm_colsum", st);
-  sp_norm_colsum_kernel<<<dim3((p.hdim + 63) / 64, 2), 256, 0, st>>>(p.partial, nblk, p.hdim, p.dgamma,
-                                                                      rms ? nullptr : p.dbeta);
-  return hipGetLastError();
+  // no rows: the column workgroups alone run and write dgamma / dbeta = 0
+  p.col_blocks = norm_bwd_col_blocks(p.hdim);
+  TraceScope ts("sp_norm_bwd", st);
+  return bf16 ? bwd_dispatch<srat::bf16>(p, rms, st) : bwd_dispatch<float>(p, rms, st);
 }
 
 hipError_t launch_hidden_mask(const NormFwdParams& p, uint8_t* mask, hipStream_t st) {

@@ -226,11 +226,12 @@ def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_dr
     else:
         dh, dy, dgamma, dbeta = outs
     if workspace is None:
-        workspace = torch.empty(max(sp_norm_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=h.device)
-    ws = workspace
+        need = sp_norm_bwd_workspace_bytes(desc)
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device) if need else None
+    ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     _check(lib().srat_sp_norm_bwd(ctypes.byref(desc), _ptr(du), _ptr(dres), _ptr(h), _ptr(gamma), _ptr(mean),
-                                  _ptr(rstd), _ptr(dh), _ptr(dy), _ptr(dgamma), _ptr(dbeta), _ptr(ws),
-                                  ws.numel(), _stream(h.device)), "srat_sp_norm_bwd")
+                                  _ptr(rstd), _ptr(dh), _ptr(dy), _ptr(dgamma), _ptr(dbeta), ws_ptr,
+                                  ws_bytes, _stream(h.device)), "srat_sp_norm_bwd")
     return dh, dy, dgamma, dbeta
 
 

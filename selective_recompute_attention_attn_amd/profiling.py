@@ -43,7 +43,6 @@ KERNEL_SOURCES = {
     "attn_bwd_gqa_sum": _BWD,
     "sp_norm_fwd": _NORM,
     "sp_norm_bwd": _NORM,
-    "sp_norm_colsum": _NORM,
 }
 
 # bench.py --calibrate-copy: each copy reads and writes this many bytes

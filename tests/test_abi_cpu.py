@@ -118,7 +118,7 @@ def test_norm_alias_rule_and_workspace(L):
     d = _ndesc()
     n = ctypes.c_size_t(0)
     assert L.srat_sp_norm_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert 0 < n.value <= 256 * 2 * 6144 * 4 + 256
+    assert n.value == 0          # dgamma / dbeta are summed without scratch memory
     p = ctypes.c_void_p(0x10000)
     rc, msg = _err(L, L.srat_sp_norm_bwd(ctypes.byref(d), p, p, p, p, p, p, p, p, p, p, p, n.value, None))
     assert rc == -1 and "alias" in msg

@@ -54,6 +54,9 @@ SHAPES = [
     (300, 2, 96, "layernorm", 0.3, "bf16"),
     (9, 2, 1000, "rmsnorm", 0.2, "fp32"),
     (600, 1, 64, "layernorm", 0.1, "fp32"),
+    (1500, 2, 256, "layernorm", 0.1, "bf16"),      # several rows per workgroup, odd remainder
+    (3, 1, 32768, "layernorm", 0.1, "bf16"),       # largest row: 4 groups per thread of 1024
+    (2, 2, 28672, "rmsnorm", 0.0, "bf16"),
 ]
 
 
@@ -109,3 +112,29 @@ def test_full_size_workload(name):
     announce(f"norm full-size {name}")
     got, ref = run_both(n, gen.norm_inputs(n), device, alias_dy=n.p_drop == 0.0)
     print(name, check(got, ref, TOL_BF16))
+
+
+def test_empty_rows_give_zero_parameter_grads():
+    device = need_gpu()
+    announce("norm empty rows")
+    h = 512
+    z = torch.empty((0, 2, h), dtype=torch.bfloat16, device=device)
+    gamma = torch.ones(h, device=device)
+    mean = torch.empty(0, device=device)
+    rstd = torch.empty(0, device=device)
+    dg = torch.full((h,), 7.0, device=device)
+    db = torch.full((h,), 7.0, device=device)
+    ops.sp_norm_bwd(z, z, z, gamma, mean, rstd, p_drop=0.1, outs=(z, torch.empty_like(z), dg, db))
+    torch.cuda.synchronize()
+    assert not dg.any() and not db.any()
+
+
+def test_parameter_grads_are_reproducible():
+    device = need_gpu()
+    n = gen.NormShape(s_local=256, b=4, h=6144, norm="layernorm", p_drop=0.1, seed=9)
+    announce("norm determinism")
+    x = gen.norm_inputs(n)
+    a, _ = run_both(n, x, device)
+    b, _ = run_both(n, x, device)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
