@@ -26,6 +26,8 @@
 //     one query per lane, so the online-softmax rescale is lane-local.
 //   * The dropout scale 1/(1-p) is applied once in the epilogue, not per
 //     element.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
@@ -40,12 +42,20 @@ constexpr int kThreads = 256;  // 4 waves
 // (log2 units): probabilities stay <= 2^8, and the O / l rescale is rare.
 constexpr float kMaxSlack = 8.0f;
 
+// Two K and two V tiles: while tile t is consumed, tile t+1 (K) / t+1 (V) are
+// already resident and the next ones are being written, so one barrier per
+// tile suffices.  K is read as 16-byte rows only (RowStride), V through the
+// transposing reads (TileStride).
 template <int D>
 struct alignas(16) FwdSmem {
-  static constexpr int kStride = TileStride<D>::kValue;
-  bf16 k[kBN * kStride];
-  bf16 v[kBN * kStride];
+  static constexpr int kKS = RowStride<D>::kValue;
+  static constexpr int kVS = TileStride<D>::kValue;
+  bf16 k[2][kBN * kKS];
+  bf16 v[2][kBN * kVS];
 };
+// two workgroups per CU where the registers of the software pipeline allow it
+template <int D>
+constexpr int fwd_occupancy() { return D <= 96 ? 2 : 1; }
 
 // MFMA row (slot) m of a 32-key block carries key perm32(m): slots
 // 8a + 4hh + jj hold keys 16hh + 4a + jj, so output register r of lane half hh
@@ -63,9 +73,21 @@ __device__ __forceinline__ int causal_tile(int rank, int nqt) {
   return rank < h ? nqt - 1 - rank : rank - h;
 }
 
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
+// Loop structure (tile t = keys 64t .. 64t+63), software-pipelined by one
+// tile inside each wave:
+//   barrier; write K[t+2], V[t+1] (fetched from global memory during tile t-1)
+//   into the free buffers; start the global loads of K[t+3], V[t+2];
+//   row max of S[t] (computed during tile t-1), rare rescale;
+//   issue the MFMAs of S[t+1] = K[t+1] Q^T   || exp / row sum / dropout of S[t]
+//   issue the MFMAs of O^T += V[t]^T P[t]^T  || Philox draws for tile t+1
+// so the matrix cores and the vector ALUs of a wave work on different tiles.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p) {
-  constexpr int kStride = FwdSmem<D>::kStride;
+__global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_kernel(AttnParams p) {
+  constexpr int kKS = FwdSmem<D>::kKS;
+  constexpr int kVS = FwdSmem<D>::kVS;
   constexpr int kDC = D / 16;        // 16-wide d chunks (QK^T k-steps)
   constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int kLoads = D / 32;     // 16-byte global loads per thread per tile (each of K, V)
@@ -79,7 +101,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const int hh_q = bh % p.hq;
   const int bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
   const int half = lane >> 5, col = lane & 31;
   const int q0 = qt * kBM;
   const int qw = q0 + 32 * wv;           // first query of this wave
@@ -107,76 +130,118 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
 
   const int nkt_all = (p.s + kBN - 1) / kBN;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
+  // tiles 0 .. n_int-1 need no masking for any query of this wave
+  const int n_int = CAUSAL ? min(p.s / kBN, (qw + 1) / kBN) : p.s / kBN;
+  // keys at or beyond key_lim are masked for this lane's query
+  const int key_lim = CAUSAL ? min(p.s, qi + 1) : p.s;
 
-  // global -> register prefetch of one K/V tile: 16-byte chunk x = tid + 256*it
+  // ---- global <-> LDS staging; chunk x = tid + 256*it of a 64 x D tile.
+  // Buffer loads: the tile's base and its valid byte count are scalars, keys
+  // at or beyond s read as zero, each chunk has a fixed 32-bit offset.
   uint4 kpre[kLoads], vpre[kLoads];
-  auto prefetch = [&](int kt) {
+  uint32_t koff[kLoads], voff[kLoads];
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      const int x = tid + kThreads * it;
-      const int key = kt * kBN + x / (D / 8);
-      const int c8 = x % (D / 8);
-      kpre[it] = make_uint4(0, 0, 0, 0);
-      vpre[it] = make_uint4(0, 0, 0, 0);
-      if (key < p.s) {
-        kpre[it] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * p.sk_s + 8 * c8);
-        vpre[it] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.sv_s + 8 * c8);
-      }
-    }
+  for (int it = 0; it < kLoads; ++it) {
+    const int x = tid + kThreads * it;
+    koff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sk_s + 8 * (x % (D / 8))) * 2);
+    voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
+  }
+  auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
+    const int rows = min(kBN, max(0, p.s - kt * kBN));
+    return (uint32_t)((int64_t)rows * stride * 2);
   };
-  auto stash = [&]() {
+  auto load_k = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kp + (int64_t)kt * kBN * p.sk_s, tile_bytes(kt, p.sk_s));
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) kpre[it] = buffer_load16(r, koff[it]);
+  };
+  auto load_v = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vp + (int64_t)kt * kBN * p.sv_s, tile_bytes(kt, p.sv_s));
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) vpre[it] = buffer_load16(r, voff[it]);
+  };
+  auto stash_k = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < kLoads; ++it) {
       const int x = tid + kThreads * it;
       const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.k[((r & ~31) | slot32(r & 31)) * kStride + 8 * c8]) = kpre[it];
-      *reinterpret_cast<uint4*>(&sm.v[r * kStride + 8 * c8]) = vpre[it];
+      *reinterpret_cast<uint4*>(&sm.k[buf][((r & ~31) | slot32(r & 31)) * kKS + 8 * c8]) = kpre[it];
+    }
+  };
+  auto stash_v = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int x = tid + kThreads * it;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<uint4*>(&sm.v[buf][r * kVS + 8 * c8]) = vpre[it];
     }
   };
 
+  const int krow = col * kKS + 8 * half;   // K tile rows are in slot order
+  const int grp = lane >> 4, lg = lane & 15;
+  const int vrow = (16 * (grp >> 1) + (lg >> 2)) * kVS + 16 * (grp & 1) + 4 * (lg & 3);
+
+  // S^T = K Q^T (raw scores) of the tile in K buffer `buf`, two 32-key blocks
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < kDC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * kb * kKS + krow + 16 * c]);
+        s[kb] = mfma32(a, qreg[c], s[kb]);
+      }
+  };
+
+  // Philox words of tile kt for this lane: call (kb, gh) covers keys
+  // 64kt + 32kb + 16half + 8gh .. +7 of query qi
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const PhiloxRow prow = philox_row((uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+  auto draws = [&](int kt, uint32_t (&w)[16]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int gh = 0; gh < 2; ++gh) {
+        const uint32_t grp8 = (uint32_t)((kt * kBN + 32 * kb + 16 * half + 8 * gh) >> 3);
+        const Philox4 rnd = philox4x32_10_row(grp8, prow);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[8 * kb + 4 * gh + j] = rnd.w[j];
+      }
+  };
+
   const uint32_t thr_hi = p.thresh << 16;
   const float c2 = p.scale_log2;
-  // LDS element offsets that do not change across tiles
-  const int krow = col * kStride + 8 * half;   // K tile rows are in slot order
-  const int grp = lane >> 4, lg = lane & 15;
-  const int vrow = (16 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
 
-  prefetch(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (kt + 1 < nkt) prefetch(kt + 1);
+  // one tile: MASK = causal / tail masking needed, NEXT = tile kt+1 exists
+  f32x16 scur[2];
+  uint32_t wcur[16];
+  auto tile = [&](int kt, auto mask_c, auto next_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
     const int key0 = kt * kBN;
-    if (CAUSAL && key0 > qw + 31) continue;   // whole tile above this wave's diagonal
-
-    // ---- S^T = K Q^T (raw scores) for two 32-key blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[32 * kb * kStride + krow + 16 * c]);
-        sacc[kb] = mfma32(a, qreg[c], sacc[kb]);
-      }
+    __syncthreads();
+    if (NEXT) {
+      stash_k(kt & 1);            // K[kt+2] over K[kt] (read during tile kt-1)
+      stash_v((kt + 1) & 1);      // V[kt+1] over V[kt-1]
+      load_k(kt + 3);
+      load_v(kt + 2);
     }
-
-    // ---- mask, tile max (raw units; the scale is positive)
-    const bool edge = (key0 + kBN > p.s) || (CAUSAL && key0 + kBN - 1 > qw);
+    // ---- mask, row max (raw units; the scale is positive)
+    if (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 16 * half + r;
+          scur[kb][r] = key >= key_lim ? -INFINITY : scur[kb][r];
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (edge) {
-          const int key = key0 + 32 * kb + 16 * half + r;
-          if (key >= p.s || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
-        }
-        mx = fmaxf(mx, sacc[kb][r]);
-      }
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c2;
     const bool grow = mx > m_use + kMaxSlack;
     if (__any(grow)) {
@@ -188,61 +253,86 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
       m_use = m_new;
     }
     const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+    // phases are kept apart (sched_barrier) so that the scheduler interleaves
+    // matrix and vector work inside each phase without hoisting the next
+    // phase's LDS reads (and their registers) into it; explicit interleave
+    // patterns inside the phases measured slower than the scheduler's own
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- p = exp2(s * c - m); row-sum of the undropped values
+    // ---- next tile's scores on the matrix cores
+    f32x16 snext[2];
+    if (NEXT) qk((kt + 1) & 1, snext);
+
+    // ---- p = exp2(s * c - m), row sum of the undropped values, dropout
+    // (1/(1-p) is applied in the epilogue), P^T as bf16 B operands
     float lsum = 0.f;
+    uint32_t pw[16];           // P^T pairs: keys 16half + r, r+1 of block kb -> pw[8kb + r/2]
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -msub));
-        sacc[kb][r] = e;
-        lsum += e;
-      }
-    }
-    l_run += lsum;
-
-    // ---- dropout: zero the dropped probabilities (1/(1-p) applied in the epilogue)
-    if (DROP) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int gh = 0; gh < 2; ++gh) {
-          const uint32_t grp8 = (uint32_t)((key0 + 32 * kb + 16 * half + 8 * gh) >> 3);
-          const Philox4 rnd = philox4x32_10(grp8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t w = rnd.w[e >> 1];
-            const bool keep = (e & 1) ? (w >= thr_hi) : ((w & 0xFFFFu) >= p.thresh);
-            sacc[kb][8 * gh + e] = keep ? sacc[kb][8 * gh + e] : 0.f;
-          }
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(scur[kb][r], c2, -msub));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(scur[kb][r + 1], c2, -msub));
+        lsum += e0;
+        lsum += e1;
+        uint32_t pk = pack_bf16x2(e0, e1);
+        if (DROP) {   // zero the dropped halves of the packed pair
+          const uint32_t w = wcur[8 * kb + (r >> 1)];
+          pk = and_or(pk, (w & 0xFFFFu) >= p.thresh ? 0xFFFFu : 0u, w >= thr_hi ? 0xFFFF0000u : 0u);
         }
+        pw[8 * kb + (r >> 1)] = pk;
       }
-    }
-
-    // ---- P^T as bf16 B operands: step c (16 keys) = block c/2, registers 8*(c%2) ..
+    l_run += lsum;
     bf16x8 pop[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[c][e] = (bf16)sacc[c >> 1][8 * (c & 1) + e];
-    }
+    for (int c = 0; c < 4; ++c)
+      pop[c] = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T; V^T operand via LDS transpose reads:
     // lane group G = lane/16 covers d = 32db + 16*(G%2) + (0..15) and the keys
     // 32*kb + 16*(G/2) + 8*c' + (0..7) of step c = 2*kb + c'.
+    const bf16* vb = sm.v[kt & 1];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kStride + vrow;
+      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kVS + vrow;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const s16x4 lo = lds_read_tr16(&sm.v[r0 + 32 * db]);
-        const s16x4 hi = lds_read_tr16(&sm.v[r0 + 4 * kStride + 32 * db]);
+        const s16x4 lo = lds_read_tr16(&vb[r0 + 32 * db]);
+        const s16x4 hi = lds_read_tr16(&vb[r0 + 4 * kVS + 32 * db]);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pop[c], oacc[db]);
       }
     }
-  }
+    if (NEXT) {
+      if (DROP) draws(kt + 1, wcur);
+      scur[0] = snext[0];
+      scur[1] = snext[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: K[0], K[1], V[0] resident, S[0] and its draws computed,
+  // K[2] and V[1] in flight
+  load_k(0);
+  load_v(0);
+  stash_k(0);
+  stash_v(0);
+  load_k(1);
+  stash_k(1);
+  __syncthreads();
+  load_k(2);
+  load_v(1);
+  qk(0, scur);
+  if (DROP) draws(0, wcur);
+
+  // separate loops (not one loop switching between tile variants): each loop
+  // body is one straight-line variant, which keeps register allocation tight
+  int kt = 0;
+  for (; kt < min(n_int, nkt - 1); ++kt) tile(kt, bool_c<false>{}, bool_c<true>{});
+  for (; kt < nkt - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
+  if (kt < n_int) tile(kt, bool_c<false>{}, bool_c<false>{});
+  else tile(kt, bool_c<true>{}, bool_c<false>{});
 
   // ---- epilogue: O = O^T / l * 1/(1-p), LSE in natural log
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);

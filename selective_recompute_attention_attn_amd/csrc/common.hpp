@@ -45,6 +45,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[1] = (bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
 }
+// a & (b | c) in one v_bitop3_b32 (truth table 0xE0 = 0xF0 & (0xCC | 0xAA)):
+// keeps the halves of a packed pair selected by the masks b (low) and c (high).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0xE0);
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -53,6 +58,24 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // D register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- buffer loads ------------------------------------------------------------
+// Raw buffer resource over `nbytes` bytes from `base` (gfx9 word 3): loads at
+// offsets >= nbytes return zero without touching memory, so a tile that runs
+// past the end of a tensor needs no branch.  Base and size MUST be
+// wave-uniform; they are moved to scalar registers explicitly (otherwise the
+// compiler may not prove it and wraps every load in a readfirstlane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(nbytes);
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0));
 }
 
 // LDS transpose read (gfx950): within each 16-lane group, lane j receives
@@ -73,6 +96,15 @@ template <int D>
 struct TileStride {
   static constexpr int kPadDwords = ((20 - (D / 2) % 32) + 32) % 32;
   static constexpr int kValue = D + 2 * kPadDwords;
+};
+
+// Row stride of a tile that is only ever read as 16-byte rows (MFMA operands
+// in row order): 4 dwords of padding, total = 4 or 20 (mod 32) dwords, also
+// measured conflict-free for that access and smaller than TileStride.
+template <int D>
+struct RowStride {
+  static_assert((D / 2) % 16 == 0, "D must be a multiple of 32");
+  static constexpr int kValue = D + 8;
 };
 
 }  // namespace srat

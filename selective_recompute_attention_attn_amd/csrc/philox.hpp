@@ -25,13 +25,10 @@ struct Philox4 {
   uint32_t w[4];
 };
 
-// a ^ b ^ k with k uniform across the wavefront: one v_bitop3_b32 (truth
-// table 0x96) on gfx950 instead of two xors.
+// a ^ b ^ k: one v_bitop3_b32 (truth table 0x96) on gfx950 instead of two xors.
 SRAT_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
 #if defined(__HIP_DEVICE_COMPILE__) && defined(__gfx950__)
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 #else
   return a ^ b ^ k;
 #endif
@@ -61,6 +58,66 @@ SRAT_HD Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3
     k1 += kWeylB;
   }
   return Philox4{{c0, c1, c2, c3}};
+}
+
+// The same generator for a fixed (c1, c2, c3) and key, with counter word c0
+// varying: the parts of rounds 1 and 2 that do not involve c0 are computed
+// once (PhiloxRow), so each call costs two multiplies and one xor fewer.
+// Bit-identical to philox4x32_10(c0, c1, c2, c3, k0, k1).
+struct PhiloxRow {
+  uint32_t f0;        // round 1: word 0 = hi(c2 * B) ^ c1 ^ k0
+  uint32_t f2;        // round 1: word 2 = hi(c0 * A) ^ f2, f2 = c3 ^ k1
+  uint32_t f5;        // round 2: word 0 = hi(w2 * B) ^ f5, f5 = lo(c2 * B) ^ (k0 + WA)
+  uint32_t f6;        // round 2: word 2 = f6 ^ lo(c0 * A), f6 = hi(f0 * A) ^ (k1 + WB)
+  uint32_t f4;        // round 2: word 3 = lo(f0 * A)
+  uint32_t k0, k1;    // key of round 3
+};
+
+SRAT_HD PhiloxRow philox_row(uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+  PhiloxRow r;
+  const uint64_t pb = (uint64_t)c2 * kMulB;
+  r.f0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
+  r.f2 = c3 ^ k1;
+  const uint64_t pa2 = (uint64_t)r.f0 * kMulA;
+  r.f5 = (uint32_t)pb ^ (k0 + kWeylA);
+  r.f6 = (uint32_t)(pa2 >> 32) ^ (k1 + kWeylB);
+  r.f4 = (uint32_t)pa2;
+  r.k0 = k0 + 2u * kWeylA;
+  r.k1 = k1 + 2u * kWeylB;
+  return r;
+}
+
+SRAT_HD Philox4 philox4x32_10_row(uint32_t c0, const PhiloxRow& f) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+  // round 1
+  const uint64_t pa = (uint64_t)c0 * kMulA;
+  const uint32_t w2 = (uint32_t)(pa >> 32) ^ f.f2;
+  // round 2 (word 1 after round 1 is lo(c2 * B), folded into f5)
+  const uint64_t pb2 = (uint64_t)w2 * kMulB;
+  uint32_t c0r = (uint32_t)(pb2 >> 32) ^ f.f5;
+  uint32_t c1r = (uint32_t)pb2;
+  uint32_t c2r = f.f6 ^ (uint32_t)pa;
+  uint32_t c3r = f.f4;
+  uint32_t k0 = f.k0, k1 = f.k1;
+#if defined(__HIPCC__)
+#pragma unroll
+#endif
+  for (int r = 2; r < 10; ++r) {
+    const uint64_t qa = (uint64_t)c0r * kMulA;
+    const uint64_t qb = (uint64_t)c2r * kMulB;
+    const uint32_t n0 = xor3((uint32_t)(qb >> 32), c1r, k0);
+    const uint32_t n2 = xor3((uint32_t)(qa >> 32), c3r, k1);
+    c1r = (uint32_t)qb;
+    c3r = (uint32_t)qa;
+    c0r = n0;
+    c2r = n2;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  return Philox4{{c0r, c1r, c2r, c3r}};
 }
 
 // Drop threshold on 16-bit draws: drop iff draw < T, T = floor(p*65536 + 1/2).

@@ -1,6 +1,7 @@
 // Host build of the library's own philox.hpp (the code the kernels use), for
 // a bit-exact check against the oracle.  Reads "seed c0 c1 c2 c3 thresh" lines,
-// prints the four words and the eight keep bits.
+// prints the four words and the eight keep bits, then the four words of the
+// row-hoisted form the kernels call.
 #include <cstdio>
 #include "philox.hpp"
 
@@ -9,8 +10,12 @@ int main() {
   while (std::scanf("%llu %llu %llu %llu %llu %llu", &seed, &c0, &c1, &c2, &c3, &t) == 6) {
     const srat::Philox4 r = srat::philox4x32_10((uint32_t)c0, (uint32_t)c1, (uint32_t)c2, (uint32_t)c3,
                                                 (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32));
-    std::printf("%08x %08x %08x %08x %02x\n", r.w[0], r.w[1], r.w[2], r.w[3],
-                srat::keep_bits8(r, (uint32_t)t));
+    // the kernels' form with the c0-independent parts of rounds 1-2 hoisted
+    const srat::PhiloxRow f = srat::philox_row((uint32_t)c1, (uint32_t)c2, (uint32_t)c3,
+                                               (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32));
+    const srat::Philox4 q = srat::philox4x32_10_row((uint32_t)c0, f);
+    std::printf("%08x %08x %08x %08x %02x %08x %08x %08x %08x\n", r.w[0], r.w[1], r.w[2], r.w[3],
+                srat::keep_bits8(r, (uint32_t)t), q.w[0], q.w[1], q.w[2], q.w[3]);
   }
   return 0;
 }

@@ -160,6 +160,7 @@ def test_library_philox_equals_oracle(philox_hpp):
             u = (int(words[e >> 1]) >> (16 * (e & 1))) & 0xFFFF
             bits |= int(u >= t) << e
         assert int(parts[4], 16) == bits
+        assert [int(x, 16) for x in parts[5:9]] == [int(w) for w in words]   # row-hoisted form
 
 
 def test_threshold_rule_matches_oracle():
