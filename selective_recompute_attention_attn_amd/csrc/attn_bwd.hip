@@ -34,6 +34,8 @@
 //         algorithmic FLOPs) but removes every atomic from the backward.
 //   gqa_sum: grouped-query attention only: dK, dV = sums over the q-heads that
 //         share a kv-head of the per-q-head fp32 partials.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
@@ -307,11 +309,15 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
 constexpr int kQM = 128;       // queries per dq workgroup
 constexpr int kQN = 64;        // keys per K/V tile
 
+// Two K and two V tiles (tile t is consumed while t+1 is written), one
+// barrier per tile.  K is read as rows (S^T = K Q^T) and transposed
+// (dQ^T += K^T dS^T): TileStride; V only as rows: RowStride.
 template <int D>
 struct alignas(16) DqSmem {
-  static constexpr int kStride = TileStride<D>::kValue;
-  bf16 k[kQN * kStride];
-  bf16 v[kQN * kStride];
+  static constexpr int kKS = TileStride<D>::kValue;
+  static constexpr int kVS = RowStride<D>::kValue;
+  bf16 k[2][kQN * kKS];
+  bf16 v[2][kQN * kVS];
 };
 
 __device__ __forceinline__ int causal_tile(int rank, int nqt) {
@@ -319,11 +325,15 @@ __device__ __forceinline__ int causal_tile(int rank, int nqt) {
   return rank < h ? nqt - 1 - rank : rank - h;
 }
 
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
 template <int D> struct DqOcc { static constexpr int kWavesPerEU = D <= 96 ? 2 : 1; };
 
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel(AttnParams p) {
-  constexpr int kStride = DqSmem<D>::kStride;
+  constexpr int kKS = DqSmem<D>::kKS;
+  constexpr int kVS = DqSmem<D>::kVS;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kLoads = D / 32;
@@ -336,7 +346,8 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int qt = CAUSAL ? causal_tile(rank, nqt) : rank;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
   const int half = lane >> 5, col = lane & 31;
   const int q0 = qt * kQM;
   const int qw = q0 + 32 * wv;
@@ -360,6 +371,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
       doreg[c] = *reinterpret_cast<const bf16x8*>(dop + (int64_t)qi * p.so_s + 16 * c + 8 * half);
     }
   }
+  // rows past s compute garbage that only reaches their own (unstored) dQ rows
   const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
   const float dlt = qvalid ? p.delta[row0 + qi] : 0.f;
 
@@ -369,98 +381,135 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
 
   const int nkt_all = (p.s + kQN - 1) / kQN;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + kQM + kQN - 1) / kQN) : nkt_all;
+  const int n_int = CAUSAL ? min(p.s / kQN, (qw + 1) / kQN) : p.s / kQN;
+  const int key_lim = CAUSAL ? min(p.s, qi + 1) : p.s;
+
+  // ---- K/V staging through buffer loads (keys past s read as zero)
   uint4 kpre[kLoads], vpre[kLoads];
-  auto prefetch = [&](int kt) {
+  uint32_t koff[kLoads], voff[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int x = tid + 256 * it;
+    koff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sk_s + 8 * (x % (D / 8))) * 2);
+    voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
+  }
+  auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
+    const int rows = min(kQN, max(0, p.s - kt * kQN));
+    return (uint32_t)((int64_t)rows * stride * 2);
+  };
+  auto load_kv = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp + (int64_t)kt * kQN * p.sk_s, tile_bytes(kt, p.sk_s));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + (int64_t)kt * kQN * p.sv_s, tile_bytes(kt, p.sv_s));
 #pragma unroll
     for (int it = 0; it < kLoads; ++it) {
-      const int x = tid + 256 * it;
-      const int key = kt * kQN + x / (D / 8);
-      const int c8 = x % (D / 8);
-      kpre[it] = vpre[it] = make_uint4(0, 0, 0, 0);
-      if (key < p.s) {
-        kpre[it] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * p.sk_s + 8 * c8);
-        vpre[it] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.sv_s + 8 * c8);
-      }
+      kpre[it] = buffer_load16(rk, koff[it]);
+      vpre[it] = buffer_load16(rv, voff[it]);
     }
   };
-  auto stash = [&]() {
+  auto stash_kv = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < kLoads; ++it) {
       const int x = tid + 256 * it;
       const int r = x / (D / 8), c8 = x % (D / 8);
-      const int row = ((r & ~31) | slot32(r & 31)) * kStride + 8 * c8;   // slot order
-      *reinterpret_cast<uint4*>(&sm.k[row]) = kpre[it];
-      *reinterpret_cast<uint4*>(&sm.v[row]) = vpre[it];
+      const int sr = (r & ~31) | slot32(r & 31);   // slot order
+      *reinterpret_cast<uint4*>(&sm.k[buf][sr * kKS + 8 * c8]) = kpre[it];
+      *reinterpret_cast<uint4*>(&sm.v[buf][sr * kVS + 8 * c8]) = vpre[it];
     }
   };
 
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const PhiloxRow prow = philox_row((uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
   const uint32_t thr_hi = p.thresh << 16;
-  const int krow = col * kStride + 8 * half;    // K, V tile rows are in slot order
+  const float c2 = p.scale_log2;
+  const int kro = col * kKS + 8 * half;    // K, V tile rows are in slot order
+  const int vro = col * kVS + 8 * half;
   // K^T operand of step c (keys 32*(c/2) + 16*h + 8*(c%2) + e of lane half h):
   // in slot order those are rows 16*(c%2) + 4*h + (0..3) and the same + 8
   const int grp = lane >> 4, lg = lane & 15;
-  const int ktr = (4 * (grp >> 1) + (lg >> 2)) * kStride + 16 * (grp & 1) + 4 * (lg & 3);
+  const int ktr = (4 * (grp >> 1) + (lg >> 2)) * kKS + 16 * (grp & 1) + 4 * (lg & 3);
 
-  prefetch(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (kt + 1 < nkt) prefetch(kt + 1);
+  auto tile = [&](int kt, auto mask_c, auto next_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
     const int key0 = kt * kQN;
-    if (CAUSAL && key0 > qw + 31) continue;   // whole tile above this wave's diagonal
-
-    // S^T = K Q^T, dP^T = V dO^T for two 32-key blocks
+    const int buf = kt & 1;
+    __syncthreads();
+    if (NEXT) {
+      stash_kv(buf ^ 1);          // K/V[kt+1] over K/V[kt-1]
+      load_kv(kt + 2);
+    }
+    // ---- S^T = K Q^T, dP^T = V dO^T for two 32-key blocks; the Philox draws
+    // of the tile are independent and overlap the MFMAs
     f32x16 sacc[2], pacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = pacc[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = pacc[kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-        const int o = 32 * kb * kStride + krow + 16 * c;
-        sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.k[o]), qreg[c], sacc[kb]);
-        pacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.v[o]), doreg[c], pacc[kb]);
+    for (int c = 0; c < kDC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * kb * kKS + kro + 16 * c]), qreg[c], sacc[kb]);
+        pacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.v[buf][32 * kb * kVS + vro + 16 * c]), doreg[c], pacc[kb]);
       }
-    }
-
-    // dS^T = P * (dP * M / (1-p) - D) as bf16 B operands (step c = block c/2, regs 8*(c%2)..)
-    const bool edge = (key0 + kQN > p.s) || (CAUSAL && key0 + kQN - 1 > qw) || !qvalid;
-    bf16x8 dsop[4];
+    uint32_t w[16];
+    if (DROP) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Philox4 rnd[2];
-      if (DROP) {
-        const uint32_t g8 = (uint32_t)((key0 + 32 * kb + 16 * half) >> 3);
-        rnd[0] = philox4x32_10(g8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
-        rnd[1] = philox4x32_10(g8 + 1, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
-      }
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -lse2));
-        if (edge) {
-          const int key = key0 + 32 * kb + 16 * half + r;
-          if (key >= p.s || (CAUSAL && key > qi) || !qvalid) pv = 0.f;
+        for (int gh = 0; gh < 2; ++gh) {
+          const Philox4 rnd = philox4x32_10_row((uint32_t)((key0 + 32 * kb + 16 * half + 8 * gh) >> 3), prow);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[8 * kb + 4 * gh + j] = rnd.w[j];
         }
-        const bool keep = DROP ? keep16(rnd, r, p.thresh, thr_hi) : true;
-        const float d = pv * fmaf(keep ? pacc[kb][r] : 0.f, p.inv_keep, -dlt);
-        dsop[2 * kb + (r >> 3)][r & 7] = (bf16)d;
-      }
     }
 
-    // dQ^T += K^T dS^T; K^T operand through LDS transpose reads
+    // ---- dS^T = P * (dP * M / (1-p) - D), packed to bf16 pairs
+    uint32_t dsw[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float pv[2], dp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + e], c2, -lse2));
+          if (MASK) pv[e] = key0 + 32 * kb + 16 * half + r + e >= key_lim ? 0.f : pv[e];
+          dp[e] = pacc[kb][r + e];
+        }
+        if (DROP) {
+          const uint32_t ww = w[8 * kb + (r >> 1)];
+          dp[0] = (ww & 0xFFFFu) >= p.thresh ? dp[0] : 0.f;
+          dp[1] = ww >= thr_hi ? dp[1] : 0.f;
+        }
+        dsw[8 * kb + (r >> 1)] =
+            pack_bf16x2(pv[0] * fmaf(dp[0], p.inv_keep, -dlt), pv[1] * fmaf(dp[1], p.inv_keep, -dlt));
+      }
+
+    // ---- dQ^T += K^T dS^T; K^T operand through LDS transpose reads
+    const bf16* kb_ = sm.k[buf];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kStride + ktr;
+      const bf16x8 dsop = __builtin_bit_cast(bf16x8, make_uint4(dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]));
+      const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kKS + ktr;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const s16x4 lo = lds_read_tr16(&sm.k[r0 + 32 * db]);
-        const s16x4 hi = lds_read_tr16(&sm.k[r0 + 8 * kStride + 32 * db]);
+        const s16x4 lo = lds_read_tr16(&kb_[r0 + 32 * db]);
+        const s16x4 hi = lds_read_tr16(&kb_[r0 + 8 * kKS + 32 * db]);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        qacc[db] = mfma32(a, dsop[c], qacc[db]);
+        qacc[db] = mfma32(a, dsop, qacc[db]);
       }
     }
-  }
+  };
+
+  // prologue: K/V[0] resident, K/V[1] in flight
+  load_kv(0);
+  stash_kv(0);
+  load_kv(1);
+  // separate straight-line loops (see the forward kernel)
+  int kt = 0;
+  for (; kt < min(n_int, nkt - 1); ++kt) tile(kt, bool_c<false>{}, bool_c<true>{});
+  for (; kt < nkt - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
+  if (kt < n_int) tile(kt, bool_c<false>{}, bool_c<false>{});
+  else tile(kt, bool_c<true>{}, bool_c<false>{});
 
   // dQ = dQ^T * scale; lane holds query qi, d = 32db + 8a + 4*half + j
   if (qvalid) {
@@ -469,10 +518,10 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     for (int db = 0; db < kDB; ++db) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        uint2 w;
-        w.x = pack_bf16x2(qacc[db][4 * a + 0] * p.scale, qacc[db][4 * a + 1] * p.scale);
-        w.y = pack_bf16x2(qacc[db][4 * a + 2] * p.scale, qacc[db][4 * a + 3] * p.scale);
-        *reinterpret_cast<uint2*>(dq + 32 * db + 8 * a + 4 * half) = w;
+        uint2 wo;
+        wo.x = pack_bf16x2(qacc[db][4 * a + 0] * p.scale, qacc[db][4 * a + 1] * p.scale);
+        wo.y = pack_bf16x2(qacc[db][4 * a + 2] * p.scale, qacc[db][4 * a + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dq + 32 * db + 8 * a + 4 * half) = wo;
       }
     }
   }
