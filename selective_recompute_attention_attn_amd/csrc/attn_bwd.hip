@@ -85,8 +85,8 @@ struct alignas(16) DkdvSmem {
   static constexpr int kRows = 32 * QH;              // queries per tile
   union {
     struct {
-      bf16 q[kRows * kS];
-      bf16 dout[kRows * kS];
+      bf16 q[2][kRows * kS];                           // two buffers: tile t read, t+1 written
+      bf16 dout[2][kRows * kS];
       bf16 pm[4 * QH][kWaveTile];
       bf16 ds[4 * QH][kWaveTile];
     } t;
@@ -96,7 +96,10 @@ struct alignas(16) DkdvSmem {
 
 // Heads with at most 96 dims: two query halves (8 waves, 2 per SIMD); larger
 // heads: one (4 waves, accumulators in AGPRs).
-template <int D> struct DkdvCfg { static constexpr int kQH = D <= 96 ? 2 : 1; };
+template <int D> struct DkdvCfg { static constexpr int kQH = D <= 64 ? 2 : 1; };
+
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
 
 template <int D, bool CAUSAL, bool DROP, bool PART>
 __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel(AttnParams p) {
@@ -115,7 +118,8 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
   const int bh = blockIdx.x % nbh;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
   const int kg = wv & 3, qh = wv >> 2;                // key group, query half
   const int half = lane >> 5, col = lane & 31;
   const int k0 = kblk * kBNk;
@@ -148,34 +152,65 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
 
   const int nqt = (p.s + kRows - 1) / kRows;
   const int qt0 = CAUSAL ? k0 / kRows : 0;
+
+  // ---- Q / dO staging through buffer loads (rows past s read as zero);
+  // chunks beyond the tile get an offset past any range
   uint4 qpre[kTileLoads], dpre[kTileLoads];
-  auto prefetch = [&](int qt) {
+  uint32_t qoff[kTileLoads], ooff[kTileLoads];
+#pragma unroll
+  for (int it = 0; it < kTileLoads; ++it) {
+    const int x = tid + kThreads * it;
+    const bool in = x < kTileChunks;
+    qoff[it] = in ? (uint32_t)(((int64_t)(x / (D / 8)) * p.sq_s + 8 * (x % (D / 8))) * 2) : 0xFFFFFFF0u;
+    ooff[it] = in ? (uint32_t)(((int64_t)(x / (D / 8)) * p.so_s + 8 * (x % (D / 8))) * 2) : 0xFFFFFFF0u;
+  }
+  auto tile_bytes = [&](int qt, int64_t stride) -> uint32_t {
+    const int rows = min(kRows, max(0, p.s - qt * kRows));
+    return (uint32_t)((int64_t)rows * stride * 2);
+  };
+  // per-row LSE / D of the lane's query (zero past s), fetched one tile ahead
+  const __amdgpu_buffer_rsrc_t rlse = buffer_rsrc(p.lse + row0, (uint32_t)p.s * 4u);
+  const __amdgpu_buffer_rsrc_t rdel = buffer_rsrc(p.delta + row0, (uint32_t)p.s * 4u);
+  float lse_n = 0.f, dlt_n = 0.f;
+  auto load_rowstats = [&](int qt) {
+    const int qo = (qt * kRows + 32 * qh + col) * 4;
+    lse_n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlse, qo, 0, 0));
+    dlt_n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdel, qo, 0, 0));
+  };
+  auto load_tile = [&](int qt) {
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qp + (int64_t)qt * kRows * p.sq_s, tile_bytes(qt, p.sq_s));
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(dop + (int64_t)qt * kRows * p.so_s, tile_bytes(qt, p.so_s));
 #pragma unroll
     for (int it = 0; it < kTileLoads; ++it) {
-      const int x = tid + kThreads * it;
-      const int r = x / (D / 8), c8 = x % (D / 8);
-      const int qrow = qt * kRows + r;
-      qpre[it] = dpre[it] = make_uint4(0, 0, 0, 0);
-      if (x < kTileChunks && qrow < p.s) {
-        qpre[it] = *reinterpret_cast<const uint4*>(qp + (int64_t)qrow * p.sq_s + 8 * c8);
-        dpre[it] = *reinterpret_cast<const uint4*>(dop + (int64_t)qrow * p.so_s + 8 * c8);
-      }
+      qpre[it] = buffer_load16(rq, qoff[it]);
+      dpre[it] = buffer_load16(ro, ooff[it]);
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < kTileLoads; ++it) {
       const int x = tid + kThreads * it;
       if (x < kTileChunks) {
         const int r = x / (D / 8), c8 = x % (D / 8);
-        *reinterpret_cast<uint4*>(&sm.t.q[r * kS + 8 * c8]) = qpre[it];
-        *reinterpret_cast<uint4*>(&sm.t.dout[r * kS + 8 * c8]) = dpre[it];
+        *reinterpret_cast<uint4*>(&sm.t.q[buf][r * kS + 8 * c8]) = qpre[it];
+        *reinterpret_cast<uint4*>(&sm.t.dout[buf][r * kS + 8 * c8]) = dpre[it];
       }
     }
   };
 
   const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
   const uint32_t thr_hi = p.thresh << 16;
+  const float c2 = p.scale_log2;
+  // the lane's two Philox calls cover keys kw0 + 16half + 8gh .. +7 of its
+  // query: fixed key group, the query varies by tile
+  // (hoisted state costs 18 registers: only where the waves have room)
+  constexpr bool kHoist = QH == 1;
+  PhiloxCol pcol[2];
+  if (DROP && kHoist) {
+#pragma unroll
+    for (int gh = 0; gh < 2; ++gh)
+      pcol[gh] = philox_col((uint32_t)((kw0 + 16 * half + 8 * gh) >> 3), hg, (uint32_t)bb, p.k0, p.k1);
+  }
   const int q_row = (32 * qh + col) * kS + 8 * half;   // this lane's Q / dO row (B operands)
   const int w_row = 512 * half + 16 * col;             // this lane's 16 keys in the wave tiles
   // (P*M)^T, dS^T A operands: lane group G reads key half G%2, query rows
@@ -184,59 +219,66 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
   const int tr_s = tr_off32(kS, lane) + 32 * qh * kS;  // dO, Q rows of this query half (B operands)
   bf16* pmt = sm.t.pm[wv];
   bf16* dst = sm.t.ds[wv];
+  const int key_l = kw0 + 16 * half;                   // the lane's first key
 
-  prefetch(qt0);
-  for (int qt = qt0; qt < nqt; ++qt) {
+  auto tile = [&](int qt, auto mask_c, auto next_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int buf = (qt - qt0) & 1;
+    const int qi = qt * kRows + 32 * qh + col;
+    const float lse2 = lse_n * kLog2e;
+    const float dlt = dlt_n;
     __syncthreads();
-    stash();
-    __syncthreads();
-    const int q0 = qt * kRows + 32 * qh;              // first query of this wave
-    const int qi = q0 + col;
-    const bool qvalid = qi < p.s;
-    const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
-    const float dlt = qvalid ? p.delta[row0 + qi] : 0.f;
-
-    // S^T = K Q^T and dP^T = V dO^T (raw, 32 keys x 32 queries)
+    if (NEXT) {
+      stash(buf ^ 1);             // Q/dO[qt+1] over Q/dO[qt-1]
+      load_rowstats(qt + 1);      // before the tile loads: waiting for it later
+      load_tile(qt + 2);          // does not wait for them
+    }
+    // S^T = K Q^T and dP^T = V dO^T (raw, 32 keys x 32 queries); the tile's
+    // Philox draws are independent and overlap the MFMAs
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    const bf16* qb_ = sm.t.q[buf];
+    const bf16* ob_ = sm.t.dout[buf];
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
-      sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&sm.t.q[q_row + 16 * c]), sacc);
-      pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&sm.t.dout[q_row + 16 * c]), pacc);
+      sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&qb_[q_row + 16 * c]), sacc);
+      pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&ob_[q_row + 16 * c]), pacc);
     }
-    if (qt + 1 < nqt) prefetch(qt + 1);
+    Philox4 rnd[2];
+    if (DROP && kHoist) {
+      rnd[0] = philox4x32_10_col((uint32_t)qi, pcol[0]);
+      rnd[1] = philox4x32_10_col((uint32_t)qi, pcol[1]);
+    } else if (DROP) {
+      const uint32_t g8 = (uint32_t)(key_l >> 3);
+      rnd[0] = philox4x32_10(g8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+      rnd[1] = philox4x32_10(g8 + 1, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+    }
+    // keys at or past kl are masked for this lane's query (all of them for a
+    // query past s)
+    const int kl = qi < p.s ? (CAUSAL ? min(p.s, qi + 1) : p.s) : 0;
 
     // recompute P, regenerate the mask, P*M and dS packed to bf16 pairs
     uint32_t pmw[8], dsw[8];
-    const bool dead = (CAUSAL && kw0 > q0 + 31) || kw0 >= p.s;   // the whole 32x32 block is masked
-    if (!dead) {
-      const bool edge = (kw0 + 32 > p.s) || (CAUSAL && kw0 + 31 > q0) || (q0 + 32 > p.s);
-      Philox4 rnd[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+      float pv[2], dp[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * r2 + e;
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, -lse2));
+        if (MASK) pv[e] = key_l + r >= kl ? 0.f : pv[e];
+        dp[e] = pacc[r];
+      }
+      uint32_t pk = pack_bf16x2(pv[0], pv[1]);
       if (DROP) {
-        const uint32_t g8 = (uint32_t)((kw0 + 16 * half) >> 3);
-        rnd[0] = philox4x32_10(g8, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
-        rnd[1] = philox4x32_10(g8 + 1, (uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+        const uint32_t w = rnd[r2 >> 2].w[r2 & 3];
+        const bool keep0 = (w & 0xFFFFu) >= p.thresh, keep1 = w >= thr_hi;
+        pk = and_or(pk, keep0 ? 0xFFFFu : 0u, keep1 ? 0xFFFF0000u : 0u);
+        dp[0] = keep0 ? dp[0] : 0.f;
+        dp[1] = keep1 ? dp[1] : 0.f;
       }
-#pragma unroll
-      for (int r2 = 0; r2 < 8; ++r2) {
-        float pk[2], dd[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * r2 + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
-          if (edge) {
-            const int key = kw0 + 16 * half + r;
-            if (key >= p.s || (CAUSAL && key > qi) || !qvalid) pv = 0.f;
-          }
-          const bool keep = DROP ? keep16(rnd, r, p.thresh, thr_hi) : true;
-          pk[e] = keep ? pv : 0.f;
-          dd[e] = pv * fmaf(keep ? pacc[r] : 0.f, p.inv_keep, -dlt);
-        }
-        pmw[r2] = pack_bf16x2(pk[0], pk[1]);
-        dsw[r2] = pack_bf16x2(dd[0], dd[1]);
-      }
-    } else {
-#pragma unroll
-      for (int r2 = 0; r2 < 8; ++r2) pmw[r2] = dsw[r2] = 0u;
+      pmw[r2] = pk;
+      dsw[r2] = pack_bf16x2(pv[0] * fmaf(dp[0], p.inv_keep, -dlt), pv[1] * fmaf(dp[1], p.inv_keep, -dlt));
     }
     *reinterpret_cast<uint4*>(&pmt[w_row]) = make_uint4(pmw[0], pmw[1], pmw[2], pmw[3]);
     *reinterpret_cast<uint4*>(&pmt[w_row + 8]) = make_uint4(pmw[4], pmw[5], pmw[6], pmw[7]);
@@ -251,11 +293,34 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
       const bf16x8 ads = tr_pair(&dst[16 * st * 16 + tr_w], 16);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        dv_acc[db] = mfma32(apm, tr_pair(&sm.t.dout[16 * st * kS + tr_s + 32 * db], kS), dv_acc[db]);
-        dk_acc[db] = mfma32(ads, tr_pair(&sm.t.q[16 * st * kS + tr_s + 32 * db], kS), dk_acc[db]);
+        dv_acc[db] = mfma32(apm, tr_pair(&ob_[16 * st * kS + tr_s + 32 * db], kS), dv_acc[db]);
+        dk_acc[db] = mfma32(ads, tr_pair(&qb_[16 * st * kS + tr_s + 32 * db], kS), dk_acc[db]);
       }
     }
+  };
+
+  // prologue: Q/dO[qt0] resident, Q/dO[qt0+1] and the row stats of qt0 in flight
+  load_tile(qt0);
+  stash(0);
+  load_rowstats(qt0);
+  load_tile(qt0 + 1);
+  // Tiles this wave computes without masking: every query of the tile at or
+  // past every key of the wave (causal) and everything inside s.
+  const int last = nqt - 1;
+  int qa = qt0, qb = qt0;
+  if (kw0 + 32 <= p.s) {
+    qa = CAUSAL ? max(qt0, (kw0 + 31 - 32 * qh + kRows - 1) / kRows) : qt0;   // first q0 >= kw0 + 31
+    qb = max(qa, (p.s - 32 * qh - 32) / kRows + 1);                            // last q0 + 31 < s
+    qb = min(qb, nqt);
+    if ((p.s - 32 * qh - 32) < 0) qb = qa;
   }
+  // separate straight-line loops (see the forward kernel)
+  int qt = qt0;
+  for (; qt < min(qa, last); ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
+  for (; qt < min(qb, last); ++qt) tile(qt, bool_c<false>{}, bool_c<true>{});
+  for (; qt < last; ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
+  if (qt >= qa && qt < qb) tile(qt, bool_c<false>{}, bool_c<false>{});
+  else tile(qt, bool_c<true>{}, bool_c<false>{});
 
   // two query halves: the second adds its share into the first through LDS
   if (QH == 2) {
@@ -324,9 +389,6 @@ __device__ __forceinline__ int causal_tile(int rank, int nqt) {
   const int h = (nqt + 1) / 2;
   return rank < h ? nqt - 1 - rank : rank - h;
 }
-
-template <bool B>
-using bool_c = std::integral_constant<bool, B>;
 
 template <int D> struct DqOcc { static constexpr int kWavesPerEU = D <= 96 ? 2 : 1; };
 

@@ -120,6 +120,76 @@ SRAT_HD Philox4 philox4x32_10_row(uint32_t c0, const PhiloxRow& f) {
   return Philox4{{c0r, c1r, c2r, c3r}};
 }
 
+// The generator for fixed (c0, c2, c3) and key with counter word c1 varying
+// (one key group, successive queries): everything of rounds 1-3 that does
+// not involve c1 is computed once (PhiloxCol).  Bit-identical to
+// philox4x32_10(c0, c1, c2, c3, k0, k1).
+struct PhiloxCol {
+  uint32_t h0;        // round 1: word 0 = c1 ^ h0,  h0 = hi(c2 * B) ^ k0
+  uint32_t r1w1;      // round 1: word 1 = lo(c2 * B)
+  uint32_t r1w3;      // round 1: word 3 = lo(c0 * A)
+  uint32_t r2w0;      // round 2: word 0 = hi(w2 * B) ^ w1 ^ k0', w2 = hi(c0 * A) ^ c3 ^ k1 (all fixed)
+  uint32_t r2w1;      // round 2: word 1 = lo(w2 * B)
+  uint32_t r3hi;      // round 3: hi(r2w0 * A) ^ k1''
+  uint32_t r3lo;      // round 3: word 3 = lo(r2w0 * A)
+  uint32_t k0, k1;    // key of round 4
+};
+
+SRAT_HD PhiloxCol philox_col(uint32_t c0, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+  PhiloxCol r;
+  const uint64_t pa = (uint64_t)c0 * kMulA;
+  const uint64_t pb = (uint64_t)c2 * kMulB;
+  r.h0 = (uint32_t)(pb >> 32) ^ k0;
+  r.r1w1 = (uint32_t)pb;
+  r.r1w3 = (uint32_t)pa;
+  const uint32_t w2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+  const uint64_t pb2 = (uint64_t)w2 * kMulB;
+  r.r2w0 = (uint32_t)(pb2 >> 32) ^ r.r1w1 ^ (k0 + kWeylA);
+  r.r2w1 = (uint32_t)pb2;
+  const uint64_t pa3 = (uint64_t)r.r2w0 * kMulA;
+  r.r3hi = (uint32_t)(pa3 >> 32) ^ (k1 + 2u * kWeylB);
+  r.r3lo = (uint32_t)pa3;
+  r.k0 = k0 + 3u * kWeylA;
+  r.k1 = k1 + 3u * kWeylB;
+  return r;
+}
+
+SRAT_HD Philox4 philox4x32_10_col(uint32_t c1, const PhiloxCol& f) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+  // round 1: only word 0 depends on c1
+  const uint32_t w0 = c1 ^ f.h0;
+  // round 2: word 0 * A varies; word 2 * B is fixed (folded into r2w0, r2w1)
+  const uint64_t pa2 = (uint64_t)w0 * kMulA;
+  const uint32_t w2 = (uint32_t)(pa2 >> 32) ^ f.r1w3 ^ (f.k1 - 2u * kWeylB);
+  const uint32_t w3 = (uint32_t)pa2;
+  // round 3: word 0 * A is fixed (r3hi, r3lo); word 2 * B varies
+  const uint64_t pb3 = (uint64_t)w2 * kMulB;
+  uint32_t c0r = xor3((uint32_t)(pb3 >> 32), f.r2w1, f.k0 - kWeylA);
+  uint32_t c1r = (uint32_t)pb3;
+  uint32_t c2r = f.r3hi ^ w3;
+  uint32_t c3r = f.r3lo;
+  uint32_t k0 = f.k0, k1 = f.k1;
+#if defined(__HIPCC__)
+#pragma unroll
+#endif
+  for (int r = 3; r < 10; ++r) {
+    const uint64_t qa = (uint64_t)c0r * kMulA;
+    const uint64_t qb = (uint64_t)c2r * kMulB;
+    const uint32_t n0 = xor3((uint32_t)(qb >> 32), c1r, k0);
+    const uint32_t n2 = xor3((uint32_t)(qa >> 32), c3r, k1);
+    c1r = (uint32_t)qb;
+    c3r = (uint32_t)qa;
+    c0r = n0;
+    c2r = n2;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  return Philox4{{c0r, c1r, c2r, c3r}};
+}
+
 // Drop threshold on 16-bit draws: drop iff draw < T, T = floor(p*65536 + 1/2).
 inline uint32_t drop_threshold16(float p) {
   return (uint32_t)((double)p * 65536.0 + 0.5);

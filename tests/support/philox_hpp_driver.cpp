@@ -1,7 +1,7 @@
 // Host build of the library's own philox.hpp (the code the kernels use), for
 // a bit-exact check against the oracle.  Reads "seed c0 c1 c2 c3 thresh" lines,
-// prints the four words and the eight keep bits, then the four words of the
-// row-hoisted form the kernels call.
+// prints the four words and the eight keep bits, then the four words of each
+// hoisted form the kernels call (fixed c1..c3; fixed c0, c2, c3).
 #include <cstdio>
 #include "philox.hpp"
 
@@ -14,8 +14,12 @@ int main() {
     const srat::PhiloxRow f = srat::philox_row((uint32_t)c1, (uint32_t)c2, (uint32_t)c3,
                                                (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32));
     const srat::Philox4 q = srat::philox4x32_10_row((uint32_t)c0, f);
-    std::printf("%08x %08x %08x %08x %02x %08x %08x %08x %08x\n", r.w[0], r.w[1], r.w[2], r.w[3],
-                srat::keep_bits8(r, (uint32_t)t), q.w[0], q.w[1], q.w[2], q.w[3]);
+    const srat::PhiloxCol fc = srat::philox_col((uint32_t)c0, (uint32_t)c2, (uint32_t)c3,
+                                                (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32));
+    const srat::Philox4 u = srat::philox4x32_10_col((uint32_t)c1, fc);
+    std::printf("%08x %08x %08x %08x %02x %08x %08x %08x %08x %08x %08x %08x %08x\n", r.w[0], r.w[1], r.w[2],
+                r.w[3], srat::keep_bits8(r, (uint32_t)t), q.w[0], q.w[1], q.w[2], q.w[3], u.w[0], u.w[1], u.w[2],
+                u.w[3]);
   }
   return 0;
 }

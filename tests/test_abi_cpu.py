@@ -161,6 +161,7 @@ def test_library_philox_equals_oracle(philox_hpp):
             bits |= int(u >= t) << e
         assert int(parts[4], 16) == bits
         assert [int(x, 16) for x in parts[5:9]] == [int(w) for w in words]   # row-hoisted form
+        assert [int(x, 16) for x in parts[9:13]] == [int(w) for w in words]  # column-hoisted form
 
 
 def test_threshold_rule_matches_oracle():
