@@ -79,31 +79,42 @@ __device__ __forceinline__ bool keep16(const Philox4 (&rnd)[2], int r, uint32_t 
 // consecutive dwords: no bank conflicts on either side.
 constexpr int kWaveTile = 32 * 32;
 
+// Configuration by head dim:
+//   d <= 64 : two query halves (8 waves, 2 per SIMD), K and V rows in registers;
+//   d == 96 : one query half (4 waves), V rows read from LDS so that a wave
+//             fits 256 registers and two workgroups share a CU;
+//   d >= 128: one query half, one workgroup per CU (accumulators in AGPRs).
+template <int D> struct DkdvCfg {
+  static constexpr int kQH = D <= 64 ? 2 : 1;
+  static constexpr bool kVLds = D == 96;
+  static constexpr int kBlocksPerCU = kVLds ? 2 : 1;
+};
+
 template <int D, int QH>
 struct alignas(16) DkdvSmem {
   static constexpr int kS = TileStride<D>::kValue;   // Q / dO tile row stride (bf16)
+  static constexpr int kVS = RowStride<D>::kValue;   // V block row stride (row reads only)
   static constexpr int kRows = 32 * QH;              // queries per tile
+  static constexpr int kVRows = DkdvCfg<D>::kVLds ? 128 : 1;
   union {
     struct {
       bf16 q[2][kRows * kS];                           // two buffers: tile t read, t+1 written
       bf16 dout[2][kRows * kS];
       bf16 pm[4 * QH][kWaveTile];
       bf16 ds[4 * QH][kWaveTile];
+      bf16 v[kVRows * kVS];                            // the block's V rows, slot order
     } t;
     float comb[4][QH == 2 ? 64 * (D / 32) * 16 : 1];   // q-half combine of one accumulator
   };
 };
 
-// Heads with at most 96 dims: two query halves (8 waves, 2 per SIMD); larger
-// heads: one (4 waves, accumulators in AGPRs).
-template <int D> struct DkdvCfg { static constexpr int kQH = D <= 64 ? 2 : 1; };
-
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
 template <int D, bool CAUSAL, bool DROP, bool PART>
-__global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel(AttnParams p) {
+__global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) void attn_bwd_dkdv_kernel(AttnParams p) {
   constexpr int QH = DkdvCfg<D>::kQH;
+  constexpr bool kVLds = DkdvCfg<D>::kVLds;
   using SM = DkdvSmem<D, QH>;
   constexpr int kS = SM::kS, kRows = SM::kRows;
   constexpr int kThreads = 256 * QH;
@@ -114,7 +125,16 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
   __shared__ SM sm;
 
   const int nbh = p.b * p.hq;
-  const int kblk = (int)(blockIdx.x / nbh);          // ascending: most queries first when causal
+  // Key-block order.  Causal, one workgroup per CU: ascending, the blocks
+  // with the most queries (lowest keys) first, the dispatcher fills in the
+  // rest.  Two per CU: the first half of the grid ascending, the second half
+  // descending, so the workgroups that share a CU (block i and i + grid/2)
+  // together carry the same number of query tiles.
+  const int nkb = (p.s + kBNk - 1) / kBNk;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int hkb = (nkb + 1) / 2;
+  const bool mirror = CAUSAL && DkdvCfg<D>::kBlocksPerCU == 2 && rank >= hkb;
+  const int kblk = mirror ? nkb - 1 - (rank - hkb) : rank;
   const int bh = blockIdx.x % nbh;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
@@ -131,8 +151,9 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
   const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
   const int64_t row0 = ((int64_t)bb * p.hq + hh_q) * p.s;
 
-  // K, V rows of this wave as MFMA A operands (rows permuted)
-  bf16x8 kreg[kDC], vreg[kDC];
+  // K (and, unless V goes through LDS, V) rows of this wave as MFMA A
+  // operands (rows permuted)
+  bf16x8 kreg[kDC], vreg[kVLds ? 1 : kDC];
   {
     const int key = kw0 + perm32(col);
     const bool ok = key < p.s;
@@ -141,11 +162,28 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
       const uint4 a = *reinterpret_cast<const uint4*>(kp + ko + 16 * c);
-      const uint4 b = *reinterpret_cast<const uint4*>(vp + vo + 16 * c);
       kreg[c] = __builtin_bit_cast(bf16x8, ok ? a : make_uint4(0, 0, 0, 0));
-      vreg[c] = __builtin_bit_cast(bf16x8, ok ? b : make_uint4(0, 0, 0, 0));
+      if (!kVLds) {
+        const uint4 b = *reinterpret_cast<const uint4*>(vp + vo + 16 * c);
+        vreg[c] = __builtin_bit_cast(bf16x8, ok ? b : make_uint4(0, 0, 0, 0));
+      }
     }
   }
+  if (kVLds) {
+    // the block's 128 V rows -> LDS in slot order (rows past s read as zero);
+    // made visible by the first tile's barrier
+    constexpr int kVS = SM::kVS;
+    const int rows = min(kBNk, p.s - k0);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + (int64_t)k0 * p.sv_s, (uint32_t)((int64_t)rows * p.sv_s * 2));
+#pragma unroll
+    for (int it = 0; it < kBNk * D / 8 / kThreads; ++it) {
+      const int x = tid + kThreads * it;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      const uint4 v4 = buffer_load16(rv, (uint32_t)(((int64_t)r * p.sv_s + 8 * c8) * 2));
+      *reinterpret_cast<uint4*>(&sm.t.v[((r & ~31) | slot32(r & 31)) * kVS + 8 * c8]) = v4;
+    }
+  }
+  const int v_row = (32 * kg + col) * SM::kVS + 8 * half;   // this lane's V row in LDS
   f32x16 dv_acc[kDB], dk_acc[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
@@ -242,7 +280,8 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, 1) void attn_bwd_dkdv_kernel
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
       sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&qb_[q_row + 16 * c]), sacc);
-      pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&ob_[q_row + 16 * c]), pacc);
+      const bf16x8 va = kVLds ? *reinterpret_cast<const bf16x8*>(&sm.t.v[v_row + 16 * c]) : vreg[kVLds ? 0 : c];
+      pacc = mfma32(va, *reinterpret_cast<const bf16x8*>(&ob_[q_row + 16 * c]), pacc);
     }
     Philox4 rnd[2];
     if (DROP && kHoist) {
