@@ -9,15 +9,19 @@ already resident in HBM.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 value       attention-core fwd+bwd algorithmic TFLOP/s, timed with HIP events
-            around the attention calls of each timed step
+            (timing-only, no system fence) around the attention calls of each
+            timed step
 roofline    the dominant kernel (largest share of the traced time): its
-            algorithmic work per launch / its mean launch time (library trace
-            events on the launch stream), against MI355X's published peak
+            algorithmic work per launch / its mean launch time, against
+            MI355X's published peak.  Launch times come from the library's
+            trace (a HIP event pair per launch, on the launch stream) in a
+            second pass over the same K steps, kept out of the timed region
 cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -123,6 +127,41 @@ def cpu_baseline(w, seconds_budget=20.0):
             "norm_gbps": gbps, "host_cores": len(os.sched_getaffinity(0))}
 
 
+class TimingEvent:
+    """HIP event used for timing only, created with hipEventDisableSystemFence:
+    recording it adds no system-scope cache writeback / invalidation between
+    the kernels it brackets (torch's events do)."""
+    _hip = None
+
+    def __init__(self, stream: int):
+        if TimingEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch has loaded
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            TimingEvent._hip = h
+        self.ev = ctypes.c_void_p()
+        self.stream = ctypes.c_void_p(stream)
+        if TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self) -> None:
+        if TimingEvent._hip.hipEventRecord(self.ev, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float(0.0)
+        if TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.ev:
+            TimingEvent._hip.hipEventDestroy(self.ev)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +169,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt22b-t8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-trace", action="store_true", help="time without per-launch trace events")
+    ap.add_argument("--no-trace", action="store_true", help="skip the traced pass (per-kernel durations)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before warmup, run COPY_CALIBRATION_REPS plain device copies of "
                          "COPY_CALIBRATION_BYTES (reference for the HBM byte counters)")
@@ -187,19 +226,30 @@ def main():
     akw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed)
     nkw = dict(norm=n.norm, p_drop=n.p_drop, seed=n.seed, site=n.site)
 
+    # every call marshalled once per buffer set: the timed loop issues one foreign
+    # call per library entry point, so the host stays ahead of the GPU
+    calls = []
+    for s in sets:
+        h, u, mu, rs = s["nf"]
+        calls.append((
+            ops.prepare_attn_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], **akw),
+            ops.prepare_attn_bwd(s["q"], s["k"], s["v"], s["o"], s["lse"], s["do"], *s["grads"], ws_attn,
+                                 **akw),
+            ops.prepare_sp_norm_fwd(s["resid"], s["y"], s["gamma"], s["beta"], h, u, mu, rs, eps=n.eps, **nkw),
+            ops.prepare_sp_norm_bwd(s["du"], s["dres"], h, s["gamma"], mu, rs, *s["nb"], ws_norm, **nkw)))
+
     def step(i, ev=None):
-        s = sets[i % N_SETS]
+        fwd, bwd, nfwd, nbwd = calls[i % N_SETS]
         if ev is not None:
             ev[0].record()
-        ops.attn_core_fwd(s["q"], s["k"], s["v"], out=s["o"], lse=s["lse"], **akw)
-        ops.attn_core_bwd(s["q"], s["k"], s["v"], s["o"], s["lse"], s["do"], workspace=ws_attn,
-                          outs=s["grads"], **akw)
+        fwd()
+        bwd()
         if ev is not None:
             ev[1].record()
-        h, u, mu, rs = ops.sp_norm_fwd(s["resid"], s["y"], s["gamma"], s["beta"], eps=n.eps, outs=s["nf"], **nkw)
+        nfwd()
         if ev is not None:
             ev[2].record()
-        ops.sp_norm_bwd(s["du"], s["dres"], h, s["gamma"], mu, rs, workspace=ws_norm, outs=s["nb"], **nkw)
+        nbwd()
         if ev is not None:
             ev[3].record()
 
@@ -213,18 +263,24 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    if not args.no_trace:
-        ops.trace_enable(True)
-        ops.trace_read(reset=True)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    evs = [[TimingEvent(stream) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # per-kernel durations come from a second pass over the same K steps with
+    # the library's launch trace on: its two events per launch add a few
+    # microseconds between kernels, so they stay out of the timed region above
     trace = {}
     if not args.no_trace:
+        ops.trace_enable(True)
+        ops.trace_read(reset=True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
         trace = ops.trace_read(reset=True)
         ops.trace_enable(False)
     ms_step = (t1 - t0) * 1e3 / args.steps

@@ -53,7 +53,9 @@ struct TraceState {
       pool.pop_back();
       return true;
     }
-    return hipEventCreate(e) == hipSuccess;
+    // timing-only events: without the system-scope fence an event record
+    // costs no cache writeback / invalidation between the traced kernels
+    return hipEventCreateWithFlags(e, hipEventDisableSystemFence) == hipSuccess;
   }
 };
 TraceState& trace() {

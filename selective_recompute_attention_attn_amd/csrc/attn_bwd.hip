@@ -14,9 +14,15 @@
 //   dQ = dS K * scale,        dK = dS^T Q * scale
 //
 // Kernels on one stream, no atomics (results are deterministic):
-//   pre : D = rowsum(dO * O) per query row.
+//   dq  : one workgroup per 128 queries, the forward's shape.  Its prologue
+//         forms D = rowsum(dO * O) for its queries (stored for dkdv); then it
+//         loops over 64-key tiles, recomputes S^T and dP^T, forms dS^T in
+//         registers and accumulates dQ^T += K^T dS^T (K^T through LDS
+//         transpose reads).  Re-doing QK^T and dO V^T here costs MFMA work
+//         (not counted in the algorithmic FLOPs) but removes every atomic
+//         from the backward.
 //   dkdv: one workgroup per (128-key block, q-head, batch).  Waves split the
-//         block's keys into four 32-key groups (and, for head dims <= 96, each
+//         block's keys into four 32-key groups (and, for head dims <= 64, each
 //         64-query tile into two 32-query halves, one wave per pair).  A wave
 //         computes S^T = K Q^T and dP^T = V dO^T with its K, V rows as
 //         register-resident MFMA A operands, rows permuted so that one lane
@@ -24,14 +30,10 @@
 //         mask (one Philox call per 8 keys) and dS are lane-local.  P*M and
 //         dS go through a wave-private LDS tile and come back transposed
 //         (ds_read_b64_tr_b16) as the A operands of dV += (P*M)^T dO and
-//         dK += dS^T Q.  Blocks are launched lowest keys first (the most
-//         queries under a causal mask) and one block per CU, so the dispatcher
-//         balances causal work.
-//   dq  : one workgroup per 128 queries, the forward's shape: it loops over
-//         64-key tiles, recomputes S^T and dP^T, forms dS^T in registers and
-//         accumulates dQ^T += K^T dS^T (K^T through LDS transpose reads).
-//         Re-doing QK^T and dO V^T here costs MFMA work (not counted in the
-//         algorithmic FLOPs) but removes every atomic from the backward.
+//         dK += dS^T Q.  Under a causal mask the blocks with the lowest keys
+//         (the most queries) are launched first; where two workgroups share
+//         a CU, the grid's second half runs in the mirrored order so that
+//         each pair carries about the same work.
 //   gqa_sum: grouped-query attention only: dK, dV = sums over the q-heads that
 //         share a kv-head of the per-q-head fp32 partials.
 #include <type_traits>
@@ -477,7 +479,21 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   }
   // rows past s compute garbage that only reaches their own (unstored) dQ rows
   const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
-  const float dlt = qvalid ? p.delta[row0 + qi] : 0.f;
+  // D = rowsum(dO * O) of the lane's query: the lane's d-slices of O against
+  // the same slices of dO (doreg), plus the other lane half's complementary
+  // slices; stored for the dK/dV kernel, which runs after this one
+  float dlt = 0.f;
+  if (qvalid) {
+    const bf16* orow = static_cast<const bf16*>(p.o) + bb * p.so_b + hh_q * p.so_h + (int64_t)qi * p.so_s;
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 16 * c + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf(bf2f(ov[e]), bf2f(doreg[c][e]), dlt);
+    }
+  }
+  dlt = halves_sum(dlt);
+  if (qvalid && half == 0) p.delta[row0 + qi] = dlt;
 
   f32x16 qacc[kDB];
 #pragma unroll
@@ -631,40 +647,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   }
 }
 
-// ============================================================== pre / gqa_sum
-// D = rowsum(dO * O) for every (b, q-head, query) row: 8 lanes per row, lane t
-// takes 8-element chunks t, t+8, ...
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnParams p) {
-  const int64_t rows = (int64_t)p.b * p.s * p.hq;            // ordered (b, s, hq)
-  const int64_t row = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
-  const int t = threadIdx.x & 7;
-  float acc = 0.f;
-  if (row < rows) {
-    const int hh = (int)(row % p.hq);
-    const int64_t bs = row / p.hq;
-    const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
-    const bf16* o = static_cast<const bf16*>(p.o) + bb * p.so_b + (int64_t)i * p.so_s + hh * p.so_h;
-    const bf16* d = static_cast<const bf16*>(p.dout) + bb * p.so_b + (int64_t)i * p.so_s + hh * p.so_h;
-    for (int c = t; c < D / 8; c += 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(o + 8 * c);
-      const uint4 b = *reinterpret_cast<const uint4*>(d + 8 * c);
-      acc += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
-             bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
-             bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
-    }
-  }
-  acc += __shfl_xor(acc, 1, kWave);
-  acc += __shfl_xor(acc, 2, kWave);
-  acc += __shfl_xor(acc, 4, kWave);
-  if (row < rows && t == 0) {
-    const int hh = (int)(row % p.hq);
-    const int64_t bs = row / p.hq;
-    const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
-    p.delta[((int64_t)bb * p.hq + hh) * p.s + i] = acc;
-  }
-}
-
+// ============================================================== gqa_sum
 // Grouped-query attention: dK, dV of a kv-head = sums over its q-heads' fp32
 // partials ([b, s, hq, d]), written as bf16 in 8-element chunks.
 template <int D>
@@ -700,29 +683,22 @@ template <int D, bool CAUSAL, bool DROP>
 hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   const bool part = p.hq != p.hkv;
   {
-    TraceScope ts("attn_bwd_dkdv", st);
-    const dim3 grid((unsigned)(((p.s + kBNk - 1) / kBNk) * p.hq * p.b));
-    const int threads = 256 * DkdvCfg<D>::kQH;
-    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
-    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
+    TraceScope ts("attn_bwd_dq", st);
+    const dim3 grid((unsigned)(((p.s + kQM - 1) / kQM) * p.hq * p.b));
+    attn_bwd_dq_kernel<D, CAUSAL, DROP><<<grid, 256, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  TraceScope ts("attn_bwd_dq", st);
-  const dim3 grid((unsigned)(((p.s + kQM - 1) / kQM) * p.hq * p.b));
-  attn_bwd_dq_kernel<D, CAUSAL, DROP><<<grid, 256, 0, st>>>(p);
+  TraceScope ts("attn_bwd_dkdv", st);
+  const dim3 grid((unsigned)(((p.s + kBNk - 1) / kBNk) * p.hq * p.b));
+  const int threads = 256 * DkdvCfg<D>::kQH;
+  if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
+  else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_launch_d(const AttnParams& p, hipStream_t st) {
-  const int64_t rows = (int64_t)p.b * p.s * p.hq;
-  {
-    TraceScope ts("attn_bwd_pre", st);
-    attn_bwd_pre_kernel<D><<<(unsigned)((rows + 31) / 32), 256, 0, st>>>(p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const bool drop = p.thresh != 0;
   hipError_t e;
   if (p.causal) e = drop ? bwd_main<D, true, true>(p, st) : bwd_main<D, true, false>(p, st);

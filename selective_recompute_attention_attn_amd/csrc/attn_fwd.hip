@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c2;
+    mx = halves_max(mx) * c2;
     const bool grow = mx > m_use + kMaxSlack;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_use;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   else tile(kt, bool_c<true>{}, bool_c<false>{});
 
   // ---- epilogue: O = O^T / l * 1/(1-p), LSE in natural log
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = halves_sum(l_run);
   if (qi < p.s) {
     const float inv = p.inv_keep / l_tot;
     bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;

@@ -37,6 +37,20 @@ __device__ __forceinline__ float wave_sum(float x) {
          (__int_as_float(__builtin_amdgcn_readlane(xi, 32)) + __int_as_float(__builtin_amdgcn_readlane(xi, 48)));
 }
 
+// Max / sum of x over lanes l and l ^ 32 (the two halves of the wave), the
+// same value in both, without an LDS round trip: v_permlane32_swap with both
+// operands x leaves the lower half's values in both halves of one result and
+// the upper half's in the other (lane order of the operands is the same in
+// both halves, so the sum is bitwise identical there).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -122,6 +122,44 @@ def attn_desc(q, k, v, o, *, causal: bool, scale: Optional[float], p_drop: float
                     seed=int(seed) & 0xFFFFFFFFFFFFFFFF, head_offset=int(head_offset))
 
 
+class Call:
+    """One library call with every argument marshalled once: descriptor, device
+    pointers, workspace and stream.  Calling it re-issues the same operation on
+    the same buffers through a single foreign call, which is what a training
+    loop that re-runs a layer on fixed buffers needs.  The object keeps the
+    tensors it was built from alive; their storage must not be resized."""
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._name = name
+        self._keep = keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc, self._name)
+
+
+def _stream_arg(device: torch.device, stream):
+    if stream is None:
+        return _stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def prepare_attn_fwd(q, k, v, o, lse, *, causal: bool = False, scale: Optional[float] = None,
+                     p_drop: float = 0.0, seed: int = 0, head_offset: int = 0, stream=None) -> Call:
+    """srat_attn_core_fwd on fixed buffers (o, lse preallocated); stream defaults to
+    torch's current stream at preparation time."""
+    b, s, hq, d = q.shape
+    if lse.shape != (b, hq, s) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise SratError("lse must be a contiguous float32 [b, hq, s] tensor")
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream_arg(q.device, stream))
+    return Call("srat_attn_core_fwd", args, (desc, q, k, v, o, lse))
+
+
 def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
                   scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
@@ -130,9 +168,8 @@ def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: 
     b, s, hq, d = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     l = torch.empty((b, hq, s), dtype=torch.float32, device=q.device) if lse is None else lse
-    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
-    _check(lib().srat_attn_core_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
-                                    _stream(q.device)), "srat_attn_core_fwd")
+    prepare_attn_fwd(q, k, v, o, l, causal=causal, scale=scale, p_drop=p_drop, seed=seed,
+                     head_offset=head_offset)()
     return o, l
 
 
@@ -143,6 +180,22 @@ def attn_bwd_workspace_bytes(desc: AttnDesc) -> int:
     return n.value
 
 
+def prepare_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, *, causal: bool = False,
+                     scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
+                     stream=None) -> Call:
+    """srat_attn_core_bwd on fixed buffers: gradients (with the strides of q, k, v)
+    and the workspace (attn_bwd_workspace_bytes) preallocated."""
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise SratError("dout must have o's shape and strides")
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise SratError("preallocated gradients must match q, k, v")
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), _stream_arg(q.device, stream))
+    return Call("srat_attn_core_bwd", args, (desc, q, k, v, o, lse, dout, dq, dk, dv, workspace))
+
+
 def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
                   p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
                   workspace: Optional[torch.Tensor] = None, outs=None):
@@ -150,24 +203,18 @@ def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optiona
 
     outs: optional preallocated (dq, dk, dv) with the strides of (q, k, v).
     """
-    if dout.shape != o.shape or dout.stride() != o.stride():
-        raise SratError("dout must have o's shape and strides")
-    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
     if outs is None:
         dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
         dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
         dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
     else:
         dq, dk, dv = outs
-        for t, ref in ((dq, q), (dk, k), (dv, v)):
-            if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
-                raise SratError("preallocated gradients must match q, k, v")
     if workspace is None:
+        desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed,
+                         head_offset=head_offset)
         workspace = torch.empty(max(attn_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=q.device)
-    ws = workspace
-    _check(lib().srat_attn_core_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                    _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
-                                    _stream(q.device)), "srat_attn_core_bwd")
+    prepare_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=causal, scale=scale, p_drop=p_drop,
+                     seed=seed, head_offset=head_offset)()
     return dq, dk, dv
 
 
@@ -181,15 +228,27 @@ def norm_desc(x: torch.Tensor, *, norm: str, eps: float, p_drop: float, seed: in
                     eps=float(eps), p_drop=float(p_drop), seed=int(seed) & 0xFFFFFFFFFFFFFFFF, site=int(site))
 
 
+def prepare_sp_norm_fwd(resid, y, gamma, beta, h, u, mean, rstd, *, norm: str = "layernorm",
+                        eps: float = 1e-5, p_drop: float = 0.0, seed: int = 0, site: int = 1,
+                        seq_offset: int = 0, stream=None) -> Call:
+    """srat_sp_norm_fwd on fixed buffers (h, u, mean, rstd preallocated; mean None for RMSNorm)."""
+    if y.shape != resid.shape or y.dtype != resid.dtype:
+        raise SratError("resid and y must match")
+    desc = norm_desc(resid, norm=norm, eps=eps, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    for t in (h, u):
+        if t.shape != resid.shape or t.dtype != resid.dtype or not t.is_contiguous():
+            raise SratError("h and u must be contiguous and match resid")
+    args = (ctypes.byref(desc), _ptr(resid), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(h), _ptr(u), _ptr(mean),
+            _ptr(rstd), _stream_arg(resid.device, stream))
+    return Call("srat_sp_norm_fwd", args, (desc, resid, y, gamma, beta, h, u, mean, rstd))
+
+
 def sp_norm_fwd(resid, y, gamma, beta=None, *, norm: str = "layernorm", eps: float = 1e-5,
                 p_drop: float = 0.0, seed: int = 0, site: int = 1, seq_offset: int = 0, outs=None):
     """h = resid + dropout(y); u = norm(h) * gamma (+ beta).  Returns h, u, mean, rstd.
 
     outs: optional preallocated (h, u, mean, rstd); mean is None for RMSNorm.
     """
-    if y.shape != resid.shape or y.dtype != resid.dtype:
-        raise SratError("resid and y must match")
-    desc = norm_desc(resid, norm=norm, eps=eps, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
     rows = resid.shape[0] * resid.shape[1]
     if outs is None:
         h = torch.empty_like(resid)
@@ -198,8 +257,8 @@ def sp_norm_fwd(resid, y, gamma, beta=None, *, norm: str = "layernorm", eps: flo
         rstd = torch.empty(rows, dtype=torch.float32, device=resid.device)
     else:
         h, u, mean, rstd = outs
-    _check(lib().srat_sp_norm_fwd(ctypes.byref(desc), _ptr(resid), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(h),
-                                  _ptr(u), _ptr(mean), _ptr(rstd), _stream(resid.device)), "srat_sp_norm_fwd")
+    prepare_sp_norm_fwd(resid, y, gamma, beta, h, u, mean, rstd, norm=norm, eps=eps, p_drop=p_drop, seed=seed,
+                        site=site, seq_offset=seq_offset)()
     return h, u, mean, rstd
 
 
@@ -209,6 +268,18 @@ def sp_norm_bwd_workspace_bytes(desc: NormDesc) -> int:
     return n.value
 
 
+def prepare_sp_norm_bwd(du, dres, h, gamma, mean, rstd, dh, dy, dgamma, dbeta, workspace=None, *,
+                        norm: str = "layernorm", p_drop: float = 0.0, seed: int = 0, site: int = 1,
+                        seq_offset: int = 0, stream=None) -> Call:
+    """srat_sp_norm_bwd on fixed buffers (dy may be dh when p_drop == 0; dbeta None for
+    RMSNorm; workspace None when sp_norm_bwd_workspace_bytes is 0)."""
+    desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
+    ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    args = (ctypes.byref(desc), _ptr(du), _ptr(dres), _ptr(h), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dh),
+            _ptr(dy), _ptr(dgamma), _ptr(dbeta), ws_ptr, ws_bytes, _stream_arg(h.device, stream))
+    return Call("srat_sp_norm_bwd", args, (desc, du, dres, h, gamma, mean, rstd, dh, dy, dgamma, dbeta, workspace))
+
+
 def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_drop: float = 0.0,
                 seed: int = 0, site: int = 1, seq_offset: int = 0, alias_dy: bool = False,
                 workspace: Optional[torch.Tensor] = None, outs=None):
@@ -216,7 +287,6 @@ def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_dr
 
     outs: optional preallocated (dh, dy, dgamma, dbeta); dy may be dh when p_drop == 0.
     """
-    desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
     hdim = h.shape[2]
     if outs is None:
         dh = torch.empty_like(h)
@@ -226,12 +296,11 @@ def sp_norm_bwd(du, dres, h, gamma, mean, rstd, *, norm: str = "layernorm", p_dr
     else:
         dh, dy, dgamma, dbeta = outs
     if workspace is None:
+        desc = norm_desc(h, norm=norm, eps=0.0, p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)
         need = sp_norm_bwd_workspace_bytes(desc)
         workspace = torch.empty(need, dtype=torch.uint8, device=h.device) if need else None
-    ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
-    _check(lib().srat_sp_norm_bwd(ctypes.byref(desc), _ptr(du), _ptr(dres), _ptr(h), _ptr(gamma), _ptr(mean),
-                                  _ptr(rstd), _ptr(dh), _ptr(dy), _ptr(dgamma), _ptr(dbeta), ws_ptr,
-                                  ws_bytes, _stream(h.device)), "srat_sp_norm_bwd")
+    prepare_sp_norm_bwd(du, dres, h, gamma, mean, rstd, dh, dy, dgamma, dbeta, workspace, norm=norm,
+                        p_drop=p_drop, seed=seed, site=site, seq_offset=seq_offset)()
     return dh, dy, dgamma, dbeta
 
 

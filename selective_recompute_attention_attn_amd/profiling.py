@@ -37,7 +37,6 @@ _NORM = [CSRC + "sp_norm.hip"] + _COMMON
 # library trace name (kernel name without "_kernel") -> the sources it is built from
 KERNEL_SOURCES = {
     "attn_fwd_bf16": [CSRC + "attn_fwd.hip"] + _COMMON,
-    "attn_bwd_pre": _BWD,
     "attn_bwd_dkdv": _BWD,
     "attn_bwd_dq": _BWD,
     "attn_bwd_gqa_sum": _BWD,
