@@ -558,6 +558,11 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
       stash_kv(buf ^ 1);          // K/V[kt+1] over K/V[kt-1]
       load_kv(kt + 2);
     }
+    // keep the loads at the top of the tile, a whole tile ahead of their use
+    // (left alone, the scheduler sinks them to the end of the loop body to
+    // reuse their registers, and the next stash waits the full load latency);
+    // at d > 96 the pinned registers cost more than the latency they hide
+    if constexpr (D <= 96) __builtin_amdgcn_sched_barrier(0);
     // ---- S^T = K Q^T, dP^T = V dO^T for two 32-key blocks; the Philox draws
     // of the tile are independent and overlap the MFMAs
     f32x16 sacc[2], pacc[2];
