@@ -22,22 +22,18 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 consecutive elements <-> fp32 registers.  NT = non-temporal (streamed
-// once: no reuse expected from the caches).
-template <bool NT = false>
+// 8 consecutive elements <-> fp32 registers (stores non-temporal: each output
+// is written once and not read back by this kernel).
 __device__ __forceinline__ void load8(const bf16* p, float v[8]) {
-  const u32x4 w = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
-                     : *reinterpret_cast<const u32x4*>(p);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
   v[0] = bf16_lo(w[0]); v[1] = bf16_hi(w[0]);
   v[2] = bf16_lo(w[1]); v[3] = bf16_hi(w[1]);
   v[4] = bf16_lo(w[2]); v[5] = bf16_hi(w[2]);
   v[6] = bf16_lo(w[3]); v[7] = bf16_hi(w[3]);
 }
-template <bool NT = false>
 __device__ __forceinline__ void load8(const float* p, float v[8]) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  const u32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
-  const u32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
+  const u32x4 a = q[0], b = q[1];
 #pragma unroll
   for (int e = 0; e < 4; ++e) { v[e] = __uint_as_float(a[e]); v[4 + e] = __uint_as_float(b[e]); }
 }
@@ -55,6 +51,48 @@ __device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
   for (int e = 0; e < 4; ++e) { a[e] = __float_as_uint(v[e]); b[e] = __float_as_uint(v[4 + e]); }
   __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
   __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(p) + 1);
+}
+
+// Raw row loads.  A row's 8-column groups are fetched as 16-byte pieces (one
+// per group for bf16, two for fp32) through a buffer resource sized to the
+// row: groups past the row's end read as zero, so the loads need no branch and
+// all of a thread's pieces are in flight before the first is used (a
+// bounds-checked load converted on the spot serialises the round trips).
+template <typename T>
+struct Piece {
+  static constexpr int kN = (int)sizeof(T) / 2;   // 16-byte pieces per 8 columns
+};
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t row, int hdim) {
+  return buffer_rsrc(static_cast<const T*>(base) + row * hdim, (uint32_t)hdim * (uint32_t)sizeof(T));
+}
+// NT: non-temporal (streamed once)
+template <typename T, bool NT>
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t r, int c, u32x4 (&w)[Piece<T>::kN]) {
+#pragma unroll
+  for (int n = 0; n < Piece<T>::kN; ++n)
+    w[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         r, (int)(16 * (Piece<T>::kN * c + n)), 0, NT ? 2 : 0));
+}
+__device__ __forceinline__ void unpack8(const u32x4 (&w)[1], float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[0][i]); v[2 * i + 1] = bf16_hi(w[0][i]); }
+}
+__device__ __forceinline__ void unpack8(const u32x4 (&w)[2], float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(w[0][i]); v[4 + i] = __uint_as_float(w[1][i]); }
+}
+
+// An fp32 [h] vector (gamma, beta) for the thread's column groups, the same way.
+template <int NIT, int BLOCK>
+__device__ __forceinline__ void load_vec(const float* v, int hdim, float (&out)[NIT][8]) {
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(v, (uint32_t)hdim * 4u);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    u32x4 w[2];
+    load_piece<float, false>(r, threadIdx.x + it * BLOCK, w);
+    unpack8(w, out[it]);
+  }
 }
 
 // Sum of `n` values per thread over the block; every thread gets the totals.
@@ -88,27 +126,26 @@ __device__ __forceinline__ void block_sum(float (&x)[N], float* red) {
 // its two reductions (mean, then the variance of the held values), and h, u
 // are streamed out with non-temporal stores.
 template <typename T, int NIT, int BLOCK>
-__device__ __forceinline__ void fwd_load(const NormFwdParams& p, int64_t row, float (&x)[NIT][8],
-                                         float (&y)[NIT][8]) {
-  const T* resid = static_cast<const T*>(p.resid) + row * p.hdim;
-  const T* yy = static_cast<const T*>(p.y) + row * p.hdim;
+__device__ __forceinline__ void fwd_load(const NormFwdParams& p, int64_t row, u32x4 (&x)[NIT][Piece<T>::kN],
+                                         u32x4 (&y)[NIT][Piece<T>::kN]) {
+  const __amdgpu_buffer_rsrc_t rx = row_rsrc<T>(p.resid, row, p.hdim);
+  const __amdgpu_buffer_rsrc_t ry = row_rsrc<T>(p.y, row, p.hdim);
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;   // 8-column group
-    if (8 * c < p.hdim) {
-      load8<true>(resid + 8 * c, x[it]);
-      load8<true>(yy + 8 * c, y[it]);
-    }
+    load_piece<T, true>(rx, c, x[it]);
+    load_piece<T, true>(ry, c, y[it]);
   }
 }
 
 // HOLD: gamma / beta come in registers (g, bt); otherwise they are loaded
 // here, next to their use (large rows, where registers are short).
 template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool HOLD>
-__device__ __forceinline__ void fwd_row(const NormFwdParams& p, int64_t row, float (&hv)[NIT][8],
-                                        const float (&yv)[NIT][8], const float (&g)[NIT][8],
+__device__ __forceinline__ void fwd_row(const NormFwdParams& p, int64_t row, const u32x4 (&xr)[NIT][Piece<T>::kN],
+                                        const u32x4 (&yr)[NIT][Piece<T>::kN], const float (&g)[NIT][8],
                                         const float (&bt)[NIT][8], float* red) {
   const int hdim = p.hdim;
+  float hv[NIT][8];
   const uint32_t bb = (uint32_t)(row % p.b);
   const uint32_t sg = (uint32_t)(p.seq_offset + row / p.b);
   float acc[1] = {0.f};
@@ -116,12 +153,15 @@ __device__ __forceinline__ void fwd_row(const NormFwdParams& p, int64_t row, flo
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;
     if (8 * c < hdim) {
+      float yv[8];
+      unpack8(xr[it], hv[it]);
+      unpack8(yr[it], yv);
       uint32_t keep = 0xFFu;
       if (DROP) keep = hidden_keep8(p.k0, p.k1, p.tag, sg, bb, (uint32_t)c, p.thresh);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float yd = ((keep >> e) & 1u) ? yv[it][e] * p.inv_keep : 0.f;
-        hv[it][e] = hv[it][e] + (DROP ? yd : yv[it][e]);
+        const float yd = ((keep >> e) & 1u) ? yv[e] * p.inv_keep : 0.f;
+        hv[it][e] = hv[it][e] + (DROP ? yd : yv[e]);
         acc[0] += RMS ? hv[it][e] * hv[it][e] : hv[it][e];
       }
     } else {
@@ -181,24 +221,20 @@ template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool PIPE>
 __global__ __launch_bounds__(BLOCK) void sp_norm_fwd_kernel(NormFwdParams p) {
   constexpr bool kHold = NIT <= 3;
   __shared__ float red[2 * (BLOCK / kWave)];
-  float g[NIT][8], bt[NIT][8];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = threadIdx.x + it * BLOCK;
-    if (kHold && 8 * c < p.hdim) {
-      load8(p.gamma + 8 * c, g[it]);
-      if (!RMS) load8(p.beta + 8 * c, bt[it]);
-    }
-  }
   const int64_t stride = gridDim.x;
   int64_t row = blockIdx.x;             // < rows: the grid never exceeds the row count
-  float xa[NIT][8], ya[NIT][8];
+  u32x4 xa[NIT][Piece<T>::kN], ya[NIT][Piece<T>::kN];
   fwd_load<T, NIT, BLOCK>(p, row, xa, ya);
+  float g[NIT][8], bt[NIT][8];
+  if (kHold) {
+    load_vec<NIT, BLOCK>(p.gamma, p.hdim, g);
+    if (!RMS) load_vec<NIT, BLOCK>(p.beta, p.hdim, bt);
+  }
   if (!PIPE) {
     fwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, row, xa, ya, g, bt, red);
     return;
   }
-  float xb[NIT][8], yb[NIT][8];
+  u32x4 xb[NIT][Piece<T>::kN], yb[NIT][Piece<T>::kN];
   while (true) {
     const int64_t r1 = row + stride;
     if (r1 < p.rows) fwd_load<T, NIT, BLOCK>(p, r1, xb, yb);
@@ -307,26 +343,25 @@ __device__ __forceinline__ void colsum_job(const NormBwdParams& p, int slab, flo
 }
 
 template <typename T, int NIT, int BLOCK>
-__device__ __forceinline__ void bwd_load(const NormBwdParams& p, int64_t row, float (&x)[NIT][8],
-                                         float (&d)[NIT][8], float (&r)[NIT][8]) {
-  const T* h = static_cast<const T*>(p.h) + row * p.hdim;
-  const T* du = static_cast<const T*>(p.du) + row * p.hdim;
-  const T* dres = static_cast<const T*>(p.dres) + row * p.hdim;
+__device__ __forceinline__ void bwd_load(const NormBwdParams& p, int64_t row, u32x4 (&x)[NIT][Piece<T>::kN],
+                                         u32x4 (&d)[NIT][Piece<T>::kN], u32x4 (&r)[NIT][Piece<T>::kN]) {
+  const __amdgpu_buffer_rsrc_t rh = row_rsrc<T>(p.h, row, p.hdim);
+  const __amdgpu_buffer_rsrc_t rd = row_rsrc<T>(p.du, row, p.hdim);
+  const __amdgpu_buffer_rsrc_t rr = row_rsrc<T>(p.dres, row, p.hdim);
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;
-    if (8 * c < p.hdim) {
-      load8(h + 8 * c, x[it]);
-      load8(du + 8 * c, d[it]);
-      load8<true>(dres + 8 * c, r[it]);
-    }
+    load_piece<T, false>(rh, c, x[it]);
+    load_piece<T, false>(rd, c, d[it]);
+    load_piece<T, true>(rr, c, r[it]);
   }
 }
 
 template <typename T, int BLOCK, int NIT, bool RMS, bool DROP, bool HOLD>
-__device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, float (&xh)[NIT][8],
-                                        float (&g)[NIT][8], const float (&dr)[NIT][8],
+__device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, const u32x4 (&xr)[NIT][Piece<T>::kN],
+                                        const u32x4 (&dur)[NIT][Piece<T>::kN], const u32x4 (&drr)[NIT][Piece<T>::kN],
                                         const float (&gam)[NIT][8], float* red) {
+  float xh[NIT][8], g[NIT][8];
   const int hdim = p.hdim;
   const float inv_n = 1.0f / (float)hdim;
   const float mu = RMS ? 0.f : p.mean[row];
@@ -338,6 +373,8 @@ __device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, flo
     if (8 * c < hdim) {
       float gl[8];
       if (!HOLD) load8(p.gamma + 8 * c, gl);
+      unpack8(xr[it], xh[it]);
+      unpack8(dur[it], g[it]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         xh[it][e] = (xh[it][e] - mu) * rs;
@@ -359,9 +396,10 @@ __device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, flo
   for (int it = 0; it < NIT; ++it) {
     const int c = threadIdx.x + it * BLOCK;
     if (8 * c < hdim) {
-      float o[8], oy[8];
+      float o[8], oy[8], dr[8];
+      unpack8(drr[it], dr);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = rs * (g[it][e] - mg - xh[it][e] * mgx) + dr[it][e];
+      for (int e = 0; e < 8; ++e) o[e] = rs * (g[it][e] - mg - xh[it][e] * mgx) + dr[e];
       store8_nt(dh + 8 * c, o);
       if (separate_dy) {
         uint32_t keep = 0xFFu;
@@ -380,14 +418,10 @@ __device__ __forceinline__ void bwd_row(const NormBwdParams& p, int64_t row, flo
 template <typename T, int BLOCK, int NIT, bool RMS, bool DROP>
 __device__ __forceinline__ void bwd_rows(const NormBwdParams& p, int64_t row, float* red) {
   constexpr bool kHold = NIT <= 3;
-  float gam[NIT][8];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = threadIdx.x + it * BLOCK;
-    if (kHold && 8 * c < p.hdim) load8(p.gamma + 8 * c, gam[it]);
-  }
-  float xa[NIT][8], da[NIT][8], ra[NIT][8];
+  u32x4 xa[NIT][Piece<T>::kN], da[NIT][Piece<T>::kN], ra[NIT][Piece<T>::kN];
   bwd_load<T, NIT, BLOCK>(p, row, xa, da, ra);
+  float gam[NIT][8];
+  if (kHold) load_vec<NIT, BLOCK>(p.gamma, p.hdim, gam);
   bwd_row<T, BLOCK, NIT, RMS, DROP, kHold>(p, row, xa, da, ra, gam, red);
 }
 
