@@ -219,3 +219,40 @@ def test_full_size_workload_sampled_heads(name):
         kv = [(0, 0)]
     ref = run_oracle(a, x, heads=heads)
     print(name, compare(got, ref, TOL_BF16, heads=heads, kv_heads=kv))
+
+
+def test_strided_views_of_a_fused_qkv_buffer():
+    """Q, K, V as views into one [b, s, 3, h, d] buffer (the layout a fused QKV
+    GEMM writes): the results equal those of contiguous copies bit for bit,
+    and dQ, dK, dV come back with the views' strides."""
+    device = need_gpu()
+    a = gen.AttnShape(b=2, s=190, hq=4, hkv=4, d=96, causal=True, p_drop=0.1, seed=11)
+    announce("strided qkv views")
+    x = gen.attn_inputs(a)
+    contiguous = run_gpu(a, x, device)
+    qkv = torch.empty((a.b, a.s, 3, a.hq, a.d), dtype=torch.bfloat16, device=device)
+    for i, n in enumerate(("q", "k", "v")):
+        qkv[:, :, i] = dev(x[n], "bf16", device)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert not q.is_contiguous()
+    do = dev(x["do"], "bf16", device)
+    kw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed, head_offset=a.head_offset)
+    o, lse = ops.attn_core_fwd(q, k, v, **kw)
+    dq, dk, dv = ops.attn_core_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    assert dq.stride() == q.stride() and dk.stride() == k.stride() and dv.stride() == v.stride()
+    for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_array_equal(host(t), contiguous[n])
+
+
+@pytest.mark.parametrize("b,s", [(0, 64), (2, 0)])
+def test_empty_batch_or_sequence(b, s):
+    """Zero-sized inputs are valid: the calls succeed, launch nothing and
+    return empty outputs."""
+    device = need_gpu()
+    announce(f"empty attention b={b} s={s}")
+    q = torch.empty((b, s, 2, 64), dtype=torch.bfloat16, device=device)
+    o, lse = ops.attn_core_fwd(q, q, q, causal=True, p_drop=0.1)
+    dq, dk, dv = ops.attn_core_bwd(q, q, q, o, lse, torch.empty_like(o), causal=True, p_drop=0.1)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and lse.shape == (b, 2, s) and dq.shape == q.shape
