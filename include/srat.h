@@ -106,8 +106,11 @@ int srat_attn_core_fwd(const srat_attn_desc* desc, const void* q, const void* k,
 
 /*
  * Workspace bytes srat_attn_core_bwd needs: the per-row D = rowsum(dO * O)
- * (4 b hq s bytes) and, for grouped-query attention only, per-q-head fp32
- * dK / dV partials (8 b s hq d bytes).  Never O(s^2).
+ * (4 b hq s bytes); for grouped-query attention, per-q-head fp32 dK / dV
+ * partials (8 b s hq d bytes); and, for causal bf16 grids too small to fill
+ * the GPU (head dim >= 128, at most 256 workgroups of 128 rows), the fp32
+ * partials of the split query tiles and key blocks (up to 24 b s hq d bytes
+ * in all).  Depends on the descriptor only.  Never O(s^2).
  */
 int srat_attn_core_bwd_workspace(const srat_attn_desc* desc, size_t* bytes);
 

@@ -113,18 +113,25 @@ srat::AttnParams attn_params(const srat_attn_desc* d) {
 }
 
 struct AttnWs {
-  size_t delta, dk_part, dv_part, total;
+  size_t delta, dk_part, dv_part, dq_part, total;
+  srat::AttnBwdSplit split;
 };
-// rowsum(dO * O) per query row, plus per-q-head fp32 dK / dV partials when
-// several q-heads share a kv-head (summed by a final kernel)
+// rowsum(dO * O) per query row; fp32 dK / dV partials when several q-heads
+// share a kv-head or key blocks are split (one slot, or two with split key
+// blocks); fp32 dQ partials (two slots) when query tiles are split
 AttnWs attn_ws(const srat_attn_desc* d) {
   AttnWs w{};
+  w.split = srat::attn_bwd_split(d->b, d->s, d->hq, d->d, d->causal != 0, d->dtype == SRAT_BF16);
   const size_t rows = (size_t)d->b * d->s * d->hq;
   size_t off = 0;
   w.delta = off; off += align256(rows * sizeof(float));
-  if (d->hq != d->hkv) {
-    w.dk_part = off; off += align256(rows * d->d * sizeof(float));
-    w.dv_part = off; off += align256(rows * d->d * sizeof(float));
+  if (d->hq != d->hkv || w.split.split_kb > 0) {
+    const size_t slots = w.split.split_kb > 0 ? 2 : 1;
+    w.dk_part = off; off += align256(slots * rows * d->d * sizeof(float));
+    w.dv_part = off; off += align256(slots * rows * d->d * sizeof(float));
+  }
+  if (w.split.split_qt > 0) {
+    w.dq_part = off; off += align256(2 * rows * d->d * sizeof(float));
   }
   w.total = off;
   return w;
@@ -236,10 +243,13 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
   p.dq = dq; p.dk = dk; p.dv = dv;
   char* base = static_cast<char*>(ws);
   p.delta = reinterpret_cast<float*>(base + w.delta);
-  if (desc->hq != desc->hkv) {
+  if (desc->hq != desc->hkv || w.split.split_kb > 0) {
     p.dk_acc = reinterpret_cast<float*>(base + w.dk_part);
     p.dv_acc = reinterpret_cast<float*>(base + w.dv_part);
   }
+  if (w.split.split_qt > 0) p.dq_part = reinterpret_cast<float*>(base + w.dq_part);
+  p.split_qt = w.split.split_qt;
+  p.split_kb = w.split.split_kb;
   hipError_t e = srat::launch_attn_bwd(p, desc->dtype == SRAT_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core_bwd launch");
   return SRAT_OK;

@@ -36,6 +36,7 @@
 //         each pair carries about the same work.
 //   gqa_sum: grouped-query attention only: dK, dV = sums over the q-heads that
 //         share a kv-head of the per-q-head fp32 partials.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -116,6 +117,11 @@ struct alignas(16) DkdvSmem {
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
+// configurations whose backward grids may be split (one workgroup per CU:
+// d >= 128; causal); elsewhere the split code compiles away
+template <int D, bool CAUSAL>
+constexpr bool kSplitBwd = CAUSAL && D >= 128;
+
 template <int D, bool CAUSAL, bool DROP, bool PART>
 __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) void attn_bwd_dkdv_kernel(AttnParams p) {
   constexpr int QH = DkdvCfg<D>::kQH;
@@ -138,8 +144,18 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   const int nkb = (p.s + kBNk - 1) / kBNk;
   const int rank = (int)(blockIdx.x / nbh);
   const int hkb = (nkb + 1) / 2;
-  const bool mirror = CAUSAL && DkdvCfg<D>::kBlocksPerCU == 2 && rank >= hkb;
-  const int kblk = mirror ? nkb - 1 - (rank - hkb) : rank;
+  // Split grids (p.split_kb > 0, causal only): the split_kb blocks with the
+  // most queries come first as two workgroups each (part 0: the first half
+  // of the block's query tiles, part 1: the rest), then the other blocks.
+  const int nsk = kSplitBwd<D, CAUSAL> ? p.split_kb : 0;
+  int kblk, part = -1;
+  if (nsk > 0) {
+    if (rank < 2 * nsk) { kblk = rank / 2; part = rank & 1; }
+    else kblk = rank - nsk;
+  } else {
+    const bool mirror = CAUSAL && DkdvCfg<D>::kBlocksPerCU == 2 && rank >= hkb;
+    kblk = mirror ? nkb - 1 - (rank - hkb) : rank;
+  }
   const int bh = blockIdx.x % nbh;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
@@ -193,8 +209,12 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
 #pragma unroll
   for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
 
-  const int nqt = (p.s + kRows - 1) / kRows;
-  const int qt0 = CAUSAL ? k0 / kRows : 0;
+  const int nqt_all = (p.s + kRows - 1) / kRows;
+  const int qt_first = CAUSAL ? k0 / kRows : 0;
+  // query tiles [qt0, nqt) of this workgroup
+  const int qt_mid = qt_first + (nqt_all - qt_first + 1) / 2;
+  const int qt0 = part == 1 ? qt_mid : qt_first;
+  const int nqt = part == 0 ? qt_mid : nqt_all;
 
   // ---- Q / dO staging through buffer loads (rows past s read as zero);
   // chunks beyond the tile get an offset past any range
@@ -402,8 +422,8 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
       const float dvv = dv_acc[db][r] * p.inv_keep;
       const float dkv = dk_acc[db][r] * p.scale;
       const int dcol = 32 * db + col;
-      if (PART) {
-        const int64_t o = (((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
+      if (PART || part >= 0) {   // slot 1 holds the second parts of split blocks
+        const int64_t o = ((int64_t)max(part, 0) * p.b * p.s * p.hq + ((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
         p.dv_acc[o] = dvv;
         p.dk_acc[o] = dkv;
       } else {
@@ -449,7 +469,17 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int nbh = p.b * p.hq;
   const int bh = blockIdx.x % nbh;
   const int rank = (int)(blockIdx.x / nbh);
-  const int qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  // Split grids (p.split_qt > 0, causal only): the split_qt longest tiles
+  // come first as two workgroups each (part 0: the first half of the tile's
+  // key tiles, part 1: the rest), then the other tiles, longest first.
+  const int nsq = kSplitBwd<D, CAUSAL> ? p.split_qt : 0;
+  int qt, part = -1;
+  if (nsq > 0) {
+    if (rank < 2 * nsq) { qt = nqt - 1 - rank / 2; part = rank & 1; }
+    else qt = nqt - 1 - (rank - nsq);
+  } else {
+    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  }
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -493,7 +523,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     }
   }
   dlt = halves_sum(dlt);
-  if (qvalid && half == 0) p.delta[row0 + qi] = dlt;
+  if (qvalid && half == 0 && part <= 0) p.delta[row0 + qi] = dlt;
 
   f32x16 qacc[kDB];
 #pragma unroll
@@ -502,6 +532,10 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int nkt_all = (p.s + kQN - 1) / kQN;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + kQM + kQN - 1) / kQN) : nkt_all;
   const int n_int = CAUSAL ? min(p.s / kQN, (qw + 1) / kQN) : p.s / kQN;
+  // key tiles [kt_lo, kt_hi) of this workgroup
+  const int kt_mid = (nkt + 1) / 2;
+  const int kt_lo = part == 1 ? kt_mid : 0;
+  const int kt_hi = part == 0 ? kt_mid : nkt;
   const int key_lim = CAUSAL ? min(p.s, qi + 1) : p.s;
 
   // ---- K/V staging through buffer loads (keys past s read as zero)
@@ -625,17 +659,30 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     }
   };
 
-  // prologue: K/V[0] resident, K/V[1] in flight
-  load_kv(0);
-  stash_kv(0);
-  load_kv(1);
+  // prologue: K/V[kt_lo] resident, K/V[kt_lo+1] in flight
+  load_kv(kt_lo);
+  stash_kv(kt_lo & 1);
+  load_kv(kt_lo + 1);
   // separate straight-line loops (see the forward kernel)
-  int kt = 0;
-  for (; kt < min(n_int, nkt - 1); ++kt) tile(kt, bool_c<false>{}, bool_c<true>{});
-  for (; kt < nkt - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
+  int kt = kt_lo;
+  for (; kt < min(n_int, kt_hi - 1); ++kt) tile(kt, bool_c<false>{}, bool_c<true>{});
+  for (; kt < kt_hi - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
   if (kt < n_int) tile(kt, bool_c<false>{}, bool_c<false>{});
   else tile(kt, bool_c<true>{}, bool_c<false>{});
 
+  // a split tile's part: the raw fp32 dQ^T partial, [2][b, hq, s, d]
+  if (part >= 0) {
+    if (qvalid) {
+      float* dst = p.dq_part + (((int64_t)part * p.b * p.hq * p.s) + row0 + qi) * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * half) =
+              make_float4(qacc[db][4 * a], qacc[db][4 * a + 1], qacc[db][4 * a + 2], qacc[db][4 * a + 3]);
+    }
+    return;
+  }
   // dQ = dQ^T * scale; lane holds query qi, d = 32db + 8a + 4*half + j
   if (qvalid) {
     bf16* dq = static_cast<bf16*>(p.dq) + bb * p.sq_b + (int64_t)qi * p.sq_s + hh_q * p.sq_h;
@@ -652,30 +699,36 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   }
 }
 
-// ============================================================== gqa_sum
-// Grouped-query attention: dK, dV of a kv-head = sums over its q-heads' fp32
-// partials ([b, s, hq, d]), written as bf16 in 8-element chunks.
+// ============================================================== partial sums
+// dK, dV of a kv-head = the sum of its fp32 partials: over the q-heads that
+// share it (grouped-query attention) and over the two parts of a split key
+// block (slot 1, keys below 128 * split_kb), in a fixed order; written as
+// bf16 in 8-element chunks.  Keys [0, nkeys) are covered.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_gqa_sum_kernel(AttnParams p) {
-  const int64_t nk = (int64_t)p.b * p.s * p.hkv * (D / 8);
+__global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnParams p, int nkeys) {
+  const int64_t nk = (int64_t)p.b * nkeys * p.hkv * (D / 8);
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= 2 * nk) return;
   const bool is_v = x >= nk;
   const int64_t y = is_v ? x - nk : x;
   const int c8 = (int)(y % (D / 8));
-  const int64_t row = y / (D / 8);                           // (b, s, hkv)
+  const int64_t row = y / (D / 8);                           // (b, key, hkv)
   const int gg = (int)(row % p.hkv);
-  const int64_t bs = row / p.hkv;
-  const int i = (int)(bs % p.s), bb = (int)(bs / p.s);
+  const int64_t bk = row / p.hkv;
+  const int i = (int)(bk % nkeys), bb = (int)(bk / nkeys);
   const int grp = p.hq / p.hkv;
-  const float* src = (is_v ? p.dv_acc : p.dk_acc) + (bs * p.hq + (int64_t)gg * grp) * D + 8 * c8;
+  const int nslot = i < 128 * p.split_kb ? 2 : 1;
+  const int64_t slot_stride = (int64_t)p.b * p.s * p.hq * D;
+  const float* src = (is_v ? p.dv_acc : p.dk_acc) + (((int64_t)bb * p.s + i) * p.hq + (int64_t)gg * grp) * D + 8 * c8;
   float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < grp; ++j) {
-    const float4 u = reinterpret_cast<const float4*>(src + (int64_t)j * D)[0];
-    const float4 v = reinterpret_cast<const float4*>(src + (int64_t)j * D)[1];
-    a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
-    a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
-  }
+  for (int sl = 0; sl < nslot; ++sl)
+    for (int j = 0; j < grp; ++j) {
+      const float* q = src + sl * slot_stride + (int64_t)j * D;
+      const float4 u = reinterpret_cast<const float4*>(q)[0];
+      const float4 v = reinterpret_cast<const float4*>(q)[1];
+      a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+      a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+    }
   uint4 w;
   w.x = pack_bf16x2(a[0], a[1]); w.y = pack_bf16x2(a[2], a[3]);
   w.z = pack_bf16x2(a[4], a[5]); w.w = pack_bf16x2(a[6], a[7]);
@@ -684,38 +737,98 @@ __global__ __launch_bounds__(256) void attn_bwd_gqa_sum_kernel(AttnParams p) {
   *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
 }
 
+// dQ of the queries of split tiles (rows from q_lo) = (part 0 + part 1) * scale.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_sum_kernel(AttnParams p, int q_lo) {
+  const int nrows = p.s - q_lo;
+  const int64_t n = (int64_t)p.b * p.hq * nrows * (D / 8);
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  const int c8 = (int)(x % (D / 8));
+  const int64_t r = x / (D / 8);                             // (b, hq, query)
+  const int qi = q_lo + (int)(r % nrows);
+  const int64_t bh = r / nrows;
+  const int hh = (int)(bh % p.hq), bb = (int)(bh / p.hq);
+  const int64_t part_stride = (int64_t)p.b * p.hq * p.s * D;
+  const float* src = p.dq_part + (bh * p.s + qi) * D + 8 * c8;
+  const float4 u0 = reinterpret_cast<const float4*>(src)[0], v0 = reinterpret_cast<const float4*>(src)[1];
+  const float4 u1 = reinterpret_cast<const float4*>(src + part_stride)[0];
+  const float4 v1 = reinterpret_cast<const float4*>(src + part_stride)[1];
+  const float sc = p.scale;
+  uint4 w;
+  w.x = pack_bf16x2((u0.x + u1.x) * sc, (u0.y + u1.y) * sc);
+  w.y = pack_bf16x2((u0.z + u1.z) * sc, (u0.w + u1.w) * sc);
+  w.z = pack_bf16x2((v0.x + v1.x) * sc, (v0.y + v1.y) * sc);
+  w.w = pack_bf16x2((v0.z + v1.z) * sc, (v0.w + v1.w) * sc);
+  bf16* dst = static_cast<bf16*>(p.dq) + bb * p.sq_b + (int64_t)qi * p.sq_s + hh * p.sq_h;
+  *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
+}
+
 template <int D, bool CAUSAL, bool DROP>
 hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   const bool part = p.hq != p.hkv;
+  const unsigned nbh = (unsigned)(p.hq * p.b);
   {
     TraceScope ts("attn_bwd_dq", st);
-    const dim3 grid((unsigned)(((p.s + kQM - 1) / kQM) * p.hq * p.b));
-    attn_bwd_dq_kernel<D, CAUSAL, DROP><<<grid, 256, 0, st>>>(p);
+    const unsigned nqt = (unsigned)((p.s + kQM - 1) / kQM);
+    attn_bwd_dq_kernel<D, CAUSAL, DROP><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  TraceScope ts("attn_bwd_dkdv", st);
-  const dim3 grid((unsigned)(((p.s + kBNk - 1) / kBNk) * p.hq * p.b));
-  const int threads = 256 * DkdvCfg<D>::kQH;
-  if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
-  else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
+  if (p.split_qt > 0) {
+    TraceScope ts("attn_bwd_dq_sum", st);
+    const int q_lo = (int)(((p.s + kQM - 1) / kQM - p.split_qt) * kQM);
+    const int64_t n = (int64_t)p.b * p.hq * (p.s - q_lo) * (D / 8);
+    attn_bwd_dq_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, q_lo);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    TraceScope ts("attn_bwd_dkdv", st);
+    const unsigned nkb = (unsigned)((p.s + kBNk - 1) / kBNk);
+    const dim3 grid((nkb + p.split_kb) * nbh);
+    const int threads = 256 * DkdvCfg<D>::kQH;
+    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
+    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!part && p.split_kb == 0) return hipSuccess;
+  TraceScope ts("attn_bwd_kv_sum", st);
+  const int nkeys = part ? p.s : min(p.s, 128 * p.split_kb);
+  const int64_t n = 2 * (int64_t)p.b * nkeys * p.hkv * (D / 8);
+  attn_bwd_kv_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, nkeys);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_launch_d(const AttnParams& p, hipStream_t st) {
   const bool drop = p.thresh != 0;
-  hipError_t e;
-  if (p.causal) e = drop ? bwd_main<D, true, true>(p, st) : bwd_main<D, true, false>(p, st);
-  else e = drop ? bwd_main<D, false, true>(p, st) : bwd_main<D, false, false>(p, st);
-  if (e != hipSuccess || p.hq == p.hkv) return e;
-  TraceScope ts("attn_bwd_gqa_sum", st);
-  const int64_t n = 2 * (int64_t)p.b * p.s * p.hkv * (D / 8);
-  attn_bwd_gqa_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p);
-  return hipGetLastError();
+  if (p.causal) return drop ? bwd_main<D, true, true>(p, st) : bwd_main<D, true, false>(p, st);
+  return drop ? bwd_main<D, false, true>(p, st) : bwd_main<D, false, false>(p, st);
 }
 
 }  // namespace
+
+AttnBwdSplit attn_bwd_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16) {
+  AttnBwdSplit r{0, 0};
+  // the one-workgroup-per-CU kernels (d >= 128) of causal grids with at most
+  // one 128-row workgroup per CU of a 256-CU MI355X
+  if (!bf16 || !causal || d < 128 || s <= 0 || b <= 0) return r;
+  const int64_t nqt = (s + kQM - 1) / kQM;
+  if (nqt * b * hq > 256) return r;
+  const int64_t nkt_all = (s + kQN - 1) / kQN;
+  for (int64_t qt = 0; qt < nqt; ++qt) {
+    const int64_t nkt = std::min(nkt_all, (qt * kQM + kQM + kQN - 1) / kQN);
+    if (nkt >= 2 && nkt > (nkt_all + 1) / 2) ++r.split_qt;
+  }
+  const int64_t nq32 = (s + 31) / 32;
+  for (int64_t kb = 0; kb < (s + kBNk - 1) / kBNk; ++kb) {
+    const int64_t len = nq32 - kb * kBNk / 32;
+    if (len >= 2 && len > (nq32 + 1) / 2) ++r.split_kb;
+  }
+  return r;
+}
 
 hipError_t launch_attn_bwd_f32(const AttnParams& p, hipStream_t st);
 

@@ -64,8 +64,9 @@ struct AttnParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dk_acc;       // grouped-query attention: [b, s, hq, d] fp32 per-q-head dK partials
+  float* dk_acc;       // fp32 dK partials [slot][b, s, hq, d] (grouped-query heads, split key blocks)
   float* dv_acc;       // ... and dV partials
+  float* dq_part;      // fp32 dQ partials [2][b, hq, s, d] of split query tiles
   float* delta;        // [b, hq, s] rowsum(dO * O)
   int64_t sq_b, sq_s, sq_h;
   int64_t sk_b, sk_s, sk_h;
@@ -79,7 +80,20 @@ struct AttnParams {
   uint32_t thresh;     // 16-bit drop threshold, 0 = no dropout
   uint32_t k0, k1;
   int32_t head_offset;
+  int32_t split_qt;    // backward: 128-query tiles whose keys are split over two dQ workgroups
+  int32_t split_kb;    // backward: 128-key blocks whose queries are split over two dK/dV workgroups
 };
+
+// Backward work split for grids too small to fill the chip (causal, one
+// workgroup per CU): the longest query tiles / key blocks are halved so that
+// no workgroup carries much more than half the longest one's work; the halves
+// write fp32 partials that a final kernel sums.  Depends on the shape only,
+// so the workspace query and the launch agree.
+struct AttnBwdSplit {
+  int32_t split_qt;
+  int32_t split_kb;
+};
+AttnBwdSplit attn_bwd_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16);
 
 hipError_t launch_attn_fwd(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnParams& p, bool bf16, hipStream_t st);
