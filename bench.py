@@ -219,6 +219,8 @@ def main():
     desc = ops.attn_desc(sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["o"], causal=a.causal,
                          scale=a.scale, p_drop=a.p_drop, seed=a.seed, head_offset=0)
     ws_attn = torch.empty(ops.attn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    need_f = ops.attn_fwd_workspace_bytes(desc)
+    ws_fwd = torch.empty(need_f, dtype=torch.uint8, device=dev) if need_f else None
     ndesc = ops.norm_desc(sets[0]["resid"], norm=n.norm, eps=n.eps, p_drop=n.p_drop, seed=n.seed, site=n.site,
                           seq_offset=0)
     need = ops.sp_norm_bwd_workspace_bytes(ndesc)
@@ -232,7 +234,7 @@ def main():
     for s in sets:
         h, u, mu, rs = s["nf"]
         calls.append((
-            ops.prepare_attn_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], **akw),
+            ops.prepare_attn_fwd(s["q"], s["k"], s["v"], s["o"], s["lse"], workspace=ws_fwd, **akw),
             ops.prepare_attn_bwd(s["q"], s["k"], s["v"], s["o"], s["lse"], s["do"], *s["grads"], ws_attn,
                                  **akw),
             ops.prepare_sp_norm_fwd(s["resid"], s["y"], s["gamma"], s["beta"], h, u, mu, rs, eps=n.eps, **nkw),

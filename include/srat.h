@@ -105,6 +105,26 @@ int srat_attn_core_fwd(const srat_attn_desc* desc, const void* q, const void* k,
                        const void* v, void* o, float* lse, void* stream);
 
 /*
+ * Workspace bytes srat_attn_core_fwd_ws can use: 0 except for causal bf16
+ * grids too small to fill the GPU (head dim >= 128, at most 256 workgroups
+ * of 128 query rows), where the longest query tiles are split over two
+ * workgroups each and need fp32 partials (8 b hq s (d + 1) bytes, rounded up
+ * to 256-byte blocks).  Depends on the descriptor only.  Never O(s^2).
+ */
+int srat_attn_core_fwd_workspace(const srat_attn_desc* desc, size_t* bytes);
+
+/*
+ * srat_attn_core_fwd with a caller-owned device workspace (256-byte aligned).
+ * With ws != NULL and a nonzero workspace query, ws_bytes must be at least
+ * that size (else SRAT_ERR_WORKSPACE) and the split grid runs: each half of
+ * a split tile writes O / l and its LSE, and a final kernel merges the halves
+ * through their LSEs.  With ws == NULL this is srat_attn_core_fwd.
+ */
+int srat_attn_core_fwd_ws(const srat_attn_desc* desc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * Workspace bytes srat_attn_core_bwd needs: the per-row D = rowsum(dO * O)
  * (4 b hq s bytes); for grouped-query attention, per-q-head fp32 dK / dV
  * partials (8 b s hq d bytes); and, for causal bf16 grids too small to fill

@@ -114,14 +114,14 @@ srat::AttnParams attn_params(const srat_attn_desc* d) {
 
 struct AttnWs {
   size_t delta, dk_part, dv_part, dq_part, total;
-  srat::AttnBwdSplit split;
+  srat::AttnSplit split;
 };
 // rowsum(dO * O) per query row; fp32 dK / dV partials when several q-heads
 // share a kv-head or key blocks are split (one slot, or two with split key
 // blocks); fp32 dQ partials (two slots) when query tiles are split
 AttnWs attn_ws(const srat_attn_desc* d) {
   AttnWs w{};
-  w.split = srat::attn_bwd_split(d->b, d->s, d->hq, d->d, d->causal != 0, d->dtype == SRAT_BF16);
+  w.split = srat::attn_grid_split(d->b, d->s, d->hq, d->d, d->causal != 0, d->dtype == SRAT_BF16);
   const size_t rows = (size_t)d->b * d->s * d->hq;
   size_t off = 0;
   w.delta = off; off += align256(rows * sizeof(float));
@@ -163,6 +163,42 @@ void norm_common(const srat_norm_desc* d, int64_t& rows, uint32_t& thresh, uint3
   k1 = (uint32_t)(d->seed >> 32);
   tag = srat::hidden_tag((uint32_t)d->site);
   inv_keep = 1.0f / (1.0f - d->p_drop);
+}
+
+// forward partials of split query tiles: O / l [2][b, hq, s, d] and LSE [2][b, hq, s], fp32
+size_t attn_fwd_ws_bytes(const srat_attn_desc* d) {
+  const srat::AttnSplit sp = srat::attn_grid_split(d->b, d->s, d->hq, d->d, d->causal != 0, d->dtype == SRAT_BF16);
+  if (sp.split_qt == 0) return 0;
+  const size_t rows = (size_t)d->b * d->hq * d->s;
+  return align256(2 * rows * d->d * sizeof(float)) + align256(2 * rows * sizeof(float));
+}
+
+int attn_fwd_impl(const srat_attn_desc* desc, const void* q, const void* k, const void* v, void* o, float* lse,
+                  void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (int e = check_attn(desc)) return e;
+  const size_t al = 16;
+  if (desc->b * desc->s > 0) {
+    if (!q || !k || !v || !o || !lse) return fail(SRAT_ERR_INVALID, "NULL tensor pointer");
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al) || !aligned(lse, 4))
+      return fail(SRAT_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  }
+  srat::AttnParams p = attn_params(desc);
+  p.q = q; p.k = k; p.v = v; p.out = o; p.lse_out = lse;
+  const size_t need = attn_fwd_ws_bytes(desc);
+  if (need > 0 && ws) {   // split grid: needs the workspace; without one, the unsplit launch
+    if (ws_bytes < need) return fail(SRAT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(SRAT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const srat::AttnSplit sp = srat::attn_grid_split(desc->b, desc->s, desc->hq, desc->d, desc->causal != 0, true);
+    const size_t rows = (size_t)desc->b * desc->hq * desc->s;
+    char* base = static_cast<char*>(ws);
+    p.o_part = reinterpret_cast<float*>(base);
+    p.lse_part = reinterpret_cast<float*>(base + align256(2 * rows * desc->d * sizeof(float)));
+    p.split_qt = sp.split_qt;
+  }
+  hipError_t e = srat::launch_attn_fwd(p, desc->dtype == SRAT_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_core_fwd launch");
+  return SRAT_OK;
 }
 
 }  // namespace
@@ -207,19 +243,20 @@ int srat_attn_core_bwd_workspace(const srat_attn_desc* desc, size_t* bytes) {
 
 int srat_attn_core_fwd(const srat_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* stream) {
+  return attn_fwd_impl(desc, q, k, v, o, lse, nullptr, 0, stream);
+}
+
+int srat_attn_core_fwd_workspace(const srat_attn_desc* desc, size_t* bytes) {
   g_err.clear();
   if (int e = check_attn(desc)) return e;
-  const size_t al = 16;
-  if (desc->b * desc->s > 0) {
-    if (!q || !k || !v || !o || !lse) return fail(SRAT_ERR_INVALID, "NULL tensor pointer");
-    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al) || !aligned(lse, 4))
-      return fail(SRAT_ERR_INVALID, "tensor pointers must be 16-byte aligned");
-  }
-  srat::AttnParams p = attn_params(desc);
-  p.q = q; p.k = k; p.v = v; p.out = o; p.lse_out = lse;
-  hipError_t e = srat::launch_attn_fwd(p, desc->dtype == SRAT_BF16, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "attn_core_fwd launch");
+  if (!bytes) return fail(SRAT_ERR_INVALID, "bytes is NULL");
+  *bytes = attn_fwd_ws_bytes(desc);
   return SRAT_OK;
+}
+
+int srat_attn_core_fwd_ws(const srat_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd_impl(desc, q, k, v, o, lse, ws, ws_bytes, stream);
 }
 
 int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k, const void* v, const void* o,

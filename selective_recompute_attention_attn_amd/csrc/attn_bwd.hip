@@ -145,13 +145,15 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   const int rank = (int)(blockIdx.x / nbh);
   const int hkb = (nkb + 1) / 2;
   // Split grids (p.split_kb > 0, causal only): the split_kb blocks with the
-  // most queries come first as two workgroups each (part 0: the first half
-  // of the block's query tiles, part 1: the rest), then the other blocks.
+  // most queries (the lowest keys) run as two workgroups each (part 0: the
+  // first half of the block's query tiles, part 1: the rest), launched in
+  // decreasing order of work.
   const int nsk = kSplitBwd<D, CAUSAL> ? p.split_kb : 0;
   int kblk, part = -1;
   if (nsk > 0) {
-    if (rank < 2 * nsk) { kblk = rank / 2; part = rank & 1; }
-    else kblk = rank - nsk;
+    int t;
+    split_order(rank, nkb, nsk, t, part);
+    kblk = nkb - 1 - t;
   } else {
     const bool mirror = CAUSAL && DkdvCfg<D>::kBlocksPerCU == 2 && rank >= hkb;
     kblk = mirror ? nkb - 1 - (rank - hkb) : rank;
@@ -470,13 +472,12 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int bh = blockIdx.x % nbh;
   const int rank = (int)(blockIdx.x / nbh);
   // Split grids (p.split_qt > 0, causal only): the split_qt longest tiles
-  // come first as two workgroups each (part 0: the first half of the tile's
-  // key tiles, part 1: the rest), then the other tiles, longest first.
+  // run as two workgroups each (part 0: the first half of the tile's key
+  // tiles, part 1: the rest), launched in decreasing order of work.
   const int nsq = kSplitBwd<D, CAUSAL> ? p.split_qt : 0;
   int qt, part = -1;
   if (nsq > 0) {
-    if (rank < 2 * nsq) { qt = nqt - 1 - rank / 2; part = rank & 1; }
-    else qt = nqt - 1 - (rank - nsq);
+    split_order(rank, nqt, nsq, qt, part);
   } else {
     qt = CAUSAL ? causal_tile(rank, nqt) : rank;
   }
@@ -810,8 +811,8 @@ hipError_t bwd_launch_d(const AttnParams& p, hipStream_t st) {
 
 }  // namespace
 
-AttnBwdSplit attn_bwd_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16) {
-  AttnBwdSplit r{0, 0};
+AttnSplit attn_grid_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16) {
+  AttnSplit r{0, 0};
   // the one-workgroup-per-CU kernels (d >= 128) of causal grids with at most
   // one 128-row workgroup per CU of a 256-CU MI355X
   if (!bf16 || !causal || d < 128 || s <= 0 || b <= 0) return r;

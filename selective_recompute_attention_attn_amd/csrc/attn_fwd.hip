@@ -76,6 +76,11 @@ __device__ __forceinline__ int causal_tile(int rank, int nqt) {
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
+// configurations whose forward grid may be split (one workgroup per CU:
+// d >= 128; causal); elsewhere the split code compiles away
+template <int D, bool CAUSAL>
+constexpr bool kSplitFwd = CAUSAL && fwd_occupancy<D>() == 1;
+
 // Loop structure (tile t = keys 64t .. 64t+63), software-pipelined by one
 // tile inside each wave:
 //   barrier; write K[t+2], V[t+1] (fetched from global memory during tile t-1)
@@ -97,7 +102,17 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   const int nbh = p.b * p.hq;
   const int bh = blockIdx.x % nbh;
   const int rank = (int)(blockIdx.x / nbh);
-  const int qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  // Split grids (p.split_qt > 0: causal, d >= 128, a workspace given): the
+  // split_qt longest tiles run as two workgroups each (part 0: the first
+  // half of the tile's key tiles, part 1: the rest); all workgroups are
+  // launched in decreasing order of work.
+  const int nsq = kSplitFwd<D, CAUSAL> ? p.split_qt : 0;
+  int qt, part = -1;
+  if (nsq > 0) {
+    split_order(rank, nqt, nsq, qt, part);
+  } else {
+    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  }
   const int hh_q = bh % p.hq;
   const int bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
@@ -129,7 +144,11 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   float l_run = 0.f;         // lane-partial row sum (this lane's keys)
 
   const int nkt_all = (p.s + kBN - 1) / kBN;
-  const int nkt = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
+  const int nkt_q = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
+  // key tiles [kt_lo, nkt) of this workgroup
+  const int kt_mid = (nkt_q + 1) / 2;
+  const int kt_lo = part == 1 ? kt_mid : 0;
+  const int nkt = part == 0 ? kt_mid : nkt_q;
   // tiles 0 .. n_int-1 need no masking for any query of this wave
   const int n_int = CAUSAL ? min(p.s / kBN, (qw + 1) / kBN) : p.s / kBN;
   // keys at or beyond key_lim are masked for this lane's query
@@ -312,23 +331,23 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: K[0], K[1], V[0] resident, S[0] and its draws computed,
-  // K[2] and V[1] in flight
-  load_k(0);
-  load_v(0);
-  stash_k(0);
-  stash_v(0);
-  load_k(1);
-  stash_k(1);
+  // ---- prologue: K[kt_lo], K[kt_lo+1], V[kt_lo] resident, S[kt_lo] and its
+  // draws computed, K[kt_lo+2] and V[kt_lo+1] in flight
+  load_k(kt_lo);
+  load_v(kt_lo);
+  stash_k(kt_lo & 1);
+  stash_v(kt_lo & 1);
+  load_k(kt_lo + 1);
+  stash_k((kt_lo + 1) & 1);
   __syncthreads();
-  load_k(2);
-  load_v(1);
-  qk(0, scur);
-  if (DROP) draws(0, wcur);
+  load_k(kt_lo + 2);
+  load_v(kt_lo + 1);
+  qk(kt_lo & 1, scur);
+  if (DROP) draws(kt_lo, wcur);
 
   // separate loops (not one loop switching between tile variants): each loop
   // body is one straight-line variant, which keeps register allocation tight
-  int kt = 0;
+  int kt = kt_lo;
   for (; kt < min(n_int, nkt - 1); ++kt) tile(kt, bool_c<false>{}, bool_c<true>{});
   for (; kt < nkt - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
   if (kt < n_int) tile(kt, bool_c<false>{}, bool_c<false>{});
@@ -336,6 +355,25 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
 
   // ---- epilogue: O = O^T / l * 1/(1-p), LSE in natural log
   const float l_tot = halves_sum(l_run);
+  if (part >= 0) {   // a split tile's part: O / l (fp32) and its LSE, merged later
+    if (qi < p.s) {
+      const int64_t row = (int64_t)part * p.b * p.hq * p.s + ((int64_t)bb * p.hq + hh_q) * p.s + qi;
+      // a row can have no visible key in one part (the first tile's early
+      // rows in part 1): O = 0 and LSE = -inf give it zero weight in the merge
+      const bool any = l_tot > 0.f;
+      const float inv = any ? 1.0f / l_tot : 0.f;
+      float* dst = p.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * half) =
+              make_float4(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
+                          oacc[db][4 * a + 3] * inv);
+      if (half == 0) p.lse_part[row] = any ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qi < p.s) {
     const float inv = p.inv_keep / l_tot;
     bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;
@@ -353,19 +391,60 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   }
 }
 
+// Merge of the two parts of a split tile's rows (from q_lo): LSE =
+// log(e^LSE0 + e^LSE1), O = (e^(LSE0-LSE) O0 + e^(LSE1-LSE) O1) / (1-p).
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnParams p, int q_lo) {
+  const int nrows = p.s - q_lo;
+  const int64_t n = (int64_t)p.b * p.hq * nrows * (D / 8);
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  const int c8 = (int)(x % (D / 8));
+  const int64_t r = x / (D / 8);                             // (b, hq, query)
+  const int qi = q_lo + (int)(r % nrows);
+  const int64_t bh = r / nrows;
+  const int hh = (int)(bh % p.hq), bb = (int)(bh / p.hq);
+  const int64_t row = bh * p.s + qi;
+  const int64_t part_rows = (int64_t)p.b * p.hq * p.s;
+  const float l0 = p.lse_part[row], l1 = p.lse_part[part_rows + row];
+  const float mx = fmaxf(l0, l1);
+  const float lse = mx + log1pf(__expf(fminf(l0, l1) - mx));
+  const float w0 = __expf(l0 - lse) * p.inv_keep, w1 = __expf(l1 - lse) * p.inv_keep;
+  const float* s0 = p.o_part + row * D + 8 * c8;
+  const float* s1 = s0 + part_rows * D;
+  const float4 a0 = reinterpret_cast<const float4*>(s0)[0], b0 = reinterpret_cast<const float4*>(s0)[1];
+  const float4 a1 = reinterpret_cast<const float4*>(s1)[0], b1 = reinterpret_cast<const float4*>(s1)[1];
+  uint4 w;
+  w.x = pack_bf16x2(w0 * a0.x + w1 * a1.x, w0 * a0.y + w1 * a1.y);
+  w.y = pack_bf16x2(w0 * a0.z + w1 * a1.z, w0 * a0.w + w1 * a1.w);
+  w.z = pack_bf16x2(w0 * b0.x + w1 * b1.x, w0 * b0.y + w1 * b1.y);
+  w.w = pack_bf16x2(w0 * b0.z + w1 * b1.z, w0 * b0.w + w1 * b1.w);
+  bf16* dst = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh * p.so_h;
+  *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
+  if (c8 == 0) p.lse_out[row] = lse;
+}
+
 template <int D>
 hipError_t fwd_launch_d(const AttnParams& p, hipStream_t st) {
   const int nqt = (p.s + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(nqt * p.hq * p.b));
+  const dim3 grid((unsigned)((nqt + p.split_qt) * p.hq * p.b));
   const bool drop = p.thresh != 0;
-  TraceScope ts("attn_fwd_bf16", st);
-  if (p.causal) {
-    if (drop) attn_fwd_bf16_kernel<D, true, true><<<grid, kThreads, 0, st>>>(p);
-    else attn_fwd_bf16_kernel<D, true, false><<<grid, kThreads, 0, st>>>(p);
-  } else {
-    if (drop) attn_fwd_bf16_kernel<D, false, true><<<grid, kThreads, 0, st>>>(p);
-    else attn_fwd_bf16_kernel<D, false, false><<<grid, kThreads, 0, st>>>(p);
+  {
+    TraceScope ts("attn_fwd_bf16", st);
+    if (p.causal) {
+      if (drop) attn_fwd_bf16_kernel<D, true, true><<<grid, kThreads, 0, st>>>(p);
+      else attn_fwd_bf16_kernel<D, true, false><<<grid, kThreads, 0, st>>>(p);
+    } else {
+      if (drop) attn_fwd_bf16_kernel<D, false, true><<<grid, kThreads, 0, st>>>(p);
+      else attn_fwd_bf16_kernel<D, false, false><<<grid, kThreads, 0, st>>>(p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.split_qt == 0) return e;
   }
+  TraceScope ts("attn_fwd_merge", st);
+  const int q_lo = (nqt - p.split_qt) * kBM;
+  const int64_t n = (int64_t)p.b * p.hq * (p.s - q_lo) * (D / 8);
+  attn_fwd_merge_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, q_lo);
   return hipGetLastError();
 }
 

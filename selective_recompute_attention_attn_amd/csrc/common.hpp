@@ -121,4 +121,27 @@ struct RowStride {
   static constexpr int kValue = D + 8;
 };
 
+// Launch order of a split grid, longest work first.  Tiles t = 0 .. n-1 are
+// modelled to take 2(t+1) units of work (a causal tile's span grows with
+// t); the top nsplit tiles run as two halves of t+1 units each.  Workgroup
+// `rank` (0 .. n + nsplit - 1) gets tile t and part 0 / 1 (a half) or -1
+// (whole), so that ranks come in decreasing modelled work: the dispatcher
+// then packs the CUs the way longest-processing-time-first scheduling does.
+// Every (tile, part) is produced by exactly one rank.  Wave-uniform.
+__device__ __forceinline__ void split_order(int rank, int n, int nsplit, int& t, int& part) {
+  int r = rank;
+  t = 0;
+  part = -1;
+  for (int len = 2 * n; len >= 1; --len) {
+    if ((len & 1) == 0 && len / 2 - 1 < n - nsplit) {   // whole tile len/2 - 1
+      if (r == 0) { t = len / 2 - 1; part = -1; return; }
+      --r;
+    }
+    if (len - 1 >= n - nsplit && len - 1 < n) {        // the halves of tile len - 1
+      if (r < 2) { t = len - 1; part = r; return; }
+      r -= 2;
+    }
+  }
+}
+
 }  // namespace srat

@@ -67,6 +67,8 @@ struct AttnParams {
   float* dk_acc;       // fp32 dK partials [slot][b, s, hq, d] (grouped-query heads, split key blocks)
   float* dv_acc;       // ... and dV partials
   float* dq_part;      // fp32 dQ partials [2][b, hq, s, d] of split query tiles
+  float* o_part;       // forward: fp32 O / l of the two parts of split query tiles [2][b, hq, s, d]
+  float* lse_part;     // forward: their LSEs [2][b, hq, s]
   float* delta;        // [b, hq, s] rowsum(dO * O)
   int64_t sq_b, sq_s, sq_h;
   int64_t sk_b, sk_s, sk_h;
@@ -80,20 +82,21 @@ struct AttnParams {
   uint32_t thresh;     // 16-bit drop threshold, 0 = no dropout
   uint32_t k0, k1;
   int32_t head_offset;
-  int32_t split_qt;    // backward: 128-query tiles whose keys are split over two dQ workgroups
+  int32_t split_qt;    // 128-query tiles whose keys are split over two workgroups (forward, dQ)
   int32_t split_kb;    // backward: 128-key blocks whose queries are split over two dK/dV workgroups
 };
 
-// Backward work split for grids too small to fill the chip (causal, one
-// workgroup per CU): the longest query tiles / key blocks are halved so that
-// no workgroup carries much more than half the longest one's work; the halves
-// write fp32 partials that a final kernel sums.  Depends on the shape only,
-// so the workspace query and the launch agree.
-struct AttnBwdSplit {
+// Work split for grids too small to fill the chip (causal, one workgroup per
+// CU): the longest query tiles / key blocks are halved so that no workgroup
+// carries much more than half the longest one's work; the halves write fp32
+// partials that a final kernel sums (dQ, dK, dV) or merges through the rows'
+// LSEs (O).  Depends on the shape only, so workspace queries and launches
+// agree.
+struct AttnSplit {
   int32_t split_qt;
   int32_t split_kb;
 };
-AttnBwdSplit attn_bwd_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16);
+AttnSplit attn_grid_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16);
 
 hipError_t launch_attn_fwd(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnParams& p, bool bf16, hipStream_t st);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsrat.so")
 SRAT_F32, SRAT_BF16 = 1, 2
 SRAT_LAYERNORM, SRAT_RMSNORM = 1, 2
 ERRORS = {-1: "SRAT_ERR_INVALID", -2: "SRAT_ERR_UNSUPPORTED", -3: "SRAT_ERR_WORKSPACE", -4: "SRAT_ERR_HIP"}
-EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_bwd", "srat_attn_core_bwd_workspace", "srat_sp_norm_fwd",
+EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_fwd_workspace", "srat_attn_core_fwd_ws", "srat_attn_core_bwd", "srat_attn_core_bwd_workspace", "srat_sp_norm_fwd",
            "srat_sp_norm_bwd", "srat_sp_norm_bwd_workspace", "srat_dropout_mask_dump", "srat_trace_enable",
            "srat_trace_read", "srat_last_error", "srat_version")
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.srat_attn_core_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp]
+        L.srat_attn_core_fwd_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
+        L.srat_attn_core_fwd_ws.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, sz, vp]
         L.srat_attn_core_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.srat_attn_core_bwd_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
         L.srat_sp_norm_fwd.argtypes = [ctypes.POINTER(NormDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -148,28 +150,46 @@ def _stream_arg(device: torch.device, stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def attn_fwd_workspace_bytes(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().srat_attn_core_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "srat_attn_core_fwd_workspace")
+    return n.value
+
+
 def prepare_attn_fwd(q, k, v, o, lse, *, causal: bool = False, scale: Optional[float] = None,
-                     p_drop: float = 0.0, seed: int = 0, head_offset: int = 0, stream=None) -> Call:
-    """srat_attn_core_fwd on fixed buffers (o, lse preallocated); stream defaults to
-    torch's current stream at preparation time."""
+                     p_drop: float = 0.0, seed: int = 0, head_offset: int = 0, workspace=None,
+                     stream=None) -> Call:
+    """srat_attn_core_fwd_ws on fixed buffers (o, lse preallocated; workspace of
+    attn_fwd_workspace_bytes or None); stream defaults to torch's current stream
+    at preparation time."""
     b, s, hq, d = q.shape
     if lse.shape != (b, hq, s) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise SratError("lse must be a contiguous float32 [b, hq, s] tensor")
     desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
-    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream_arg(q.device, stream))
-    return Call("srat_attn_core_fwd", args, (desc, q, k, v, o, lse))
+    ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), ws_ptr, ws_bytes,
+            _stream_arg(q.device, stream))
+    return Call("srat_attn_core_fwd_ws", args, (desc, q, k, v, o, lse, workspace))
 
 
 def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
                   scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
-                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
-                  ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O = dropout(softmax(q k^T * scale)) v and the per-row LSE [b, hq, s] (fp32)."""
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = dropout(softmax(q k^T * scale)) v and the per-row LSE [b, hq, s] (fp32).
+
+    workspace: None allocates the one the shape can use (none for most shapes).
+    """
     b, s, hq, d = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     l = torch.empty((b, hq, s), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        need = attn_fwd_workspace_bytes(attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop,
+                                                  seed=seed, head_offset=head_offset))
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     prepare_attn_fwd(q, k, v, o, l, causal=causal, scale=scale, p_drop=p_drop, seed=seed,
-                     head_offset=head_offset)()
+                     head_offset=head_offset, workspace=workspace)()
     return o, l
 
 

@@ -256,3 +256,26 @@ def test_empty_batch_or_sequence(b, s):
     dq, dk, dv = ops.attn_core_bwd(q, q, q, o, lse, torch.empty_like(o), causal=True, p_drop=0.1)
     torch.cuda.synchronize()
     assert o.shape == q.shape and lse.shape == (b, 2, s) and dq.shape == q.shape
+
+
+def test_forward_split_grid_and_unsplit_agree_with_the_oracle():
+    """A small causal grid at d = 128 can split its longest query tiles over
+    two workgroups (with a workspace) or not (without one): both match the
+    oracle, and the merged LSE equals the unsplit one to fp32 rounding."""
+    device = need_gpu()
+    a = gen.AttnShape(b=1, s=384, hq=4, hkv=2, d=128, causal=True, p_drop=0.1, seed=21)
+    announce("forward split vs unsplit")
+    x = gen.attn_inputs(a)
+    q, k, v = (dev(x[n], "bf16", device) for n in ("q", "k", "v"))
+    kw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed, head_offset=a.head_offset)
+    o1 = torch.empty_like(q)
+    l1 = torch.empty((a.b, a.hq, a.s), dtype=torch.float32, device=device)
+    desc = ops.attn_desc(q, k, v, o1, head_offset=0, **{n: kw[n] for n in ("causal", "scale", "p_drop", "seed")})
+    assert ops.attn_fwd_workspace_bytes(desc) > 0
+    ops.prepare_attn_fwd(q, k, v, o1, l1, workspace=None, **kw)()          # unsplit
+    o2, l2 = ops.attn_core_fwd(q, k, v, **kw)                              # split (workspace allocated)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oat.attn_fwd(x["q"], x["k"], x["v"], **kw)
+    assert_close("o unsplit", host(o1), o_ref, TOL_BF16)
+    assert_close("o split", host(o2), o_ref, TOL_BF16)
+    np.testing.assert_allclose(host(l2), host(l1), rtol=1e-5, atol=1e-5)
