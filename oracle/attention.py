@@ -29,6 +29,12 @@ of a kv-head sum the contributions of its q-heads.
 
 Layouts: Q, O, dO, dQ ``[b, s, hq, d]``; K, V, dK, dV ``[b, s, hkv, d]``;
 LSE ``[b, hq, s]``.  All arithmetic in float64.
+
+Padded batches: with ``seqlens`` (one valid length L_b <= s per batch
+element) the core acts on the first L_b positions of each element only, as
+if the sequence were that long -- keys at or past L_b are invisible, the
+dropout mask keeps its global (row, column) counters -- and the padded
+positions get O = 0, LSE = -inf and zero gradients.
 """
 from __future__ import annotations
 
@@ -64,21 +70,34 @@ def softmax_rows(S):
     return E / l, (m + np.log(l))[:, 0]
 
 
-def attn_fwd(q, k, v, *, causal, scale, p_drop, seed, head_offset=0, heads=None):
-    """O and LSE.  `heads` optionally restricts the work to [(bb, hh), ...]."""
+def _lengths(seqlens, b, s):
+    if seqlens is None:
+        return [s] * b
+    L = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    if len(L) != b or any(x < 0 or x > s for x in L):
+        raise ValueError("seqlens must hold b lengths in [0, s]")
+    return L
+
+
+def attn_fwd(q, k, v, *, causal, scale, p_drop, seed, head_offset=0, heads=None, seqlens=None):
+    """O and LSE.  `heads` optionally restricts the work to [(bb, hh), ...];
+    `seqlens` gives each batch element's valid length (padded batch)."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     b, s, hq, hkv, d = _check(q, k, v)
+    lens = _lengths(seqlens, b, s)
     grp = hq // hkv
     O = np.zeros((b, s, hq, d))
-    LSE = np.zeros((b, hq, s))
+    LSE = np.full((b, hq, s), -np.inf)
     todo = heads if heads is not None else [(bb, hh) for bb in range(b) for hh in range(hq)]
     for bb, hh in todo:
-        g = hh // grp
-        P, lse = softmax_rows(scores(q[bb, :, hh], k[bb, :, g], scale, causal))
-        M = attn_keep_mask(seed, p_drop, bb, head_offset + hh, s, s)
+        g, L = hh // grp, lens[bb]
+        if L == 0:
+            continue
+        P, lse = softmax_rows(scores(q[bb, :L, hh], k[bb, :L, g], scale, causal))
+        M = attn_keep_mask(seed, p_drop, bb, head_offset + hh, L, L)
         Pd = P * M / (1.0 - p_drop)
-        O[bb, :, hh] = Pd @ v[bb, :, g]
-        LSE[bb, hh] = lse
+        O[bb, :L, hh] = Pd @ v[bb, :L, g]
+        LSE[bb, hh, :L] = lse
     return O, LSE
 
 
@@ -91,28 +110,31 @@ def attn_probs(q, k, *, causal, scale, bb, hh, hkv_index=None):
 
 
 def attn_bwd(q, k, v, lse, do, *, causal, scale, p_drop, seed, head_offset=0,
-             heads=None):
+             heads=None, seqlens=None):
     """dQ, dK, dV by recomputation: P = exp(S - LSE), M regenerated from Philox.
 
     This is the selective-recompute backward: neither P nor M is an input.
-    `lse` is the forward's LSE (``[b, hq, s]``).
+    `lse` is the forward's LSE (``[b, hq, s]``); `seqlens` as in attn_fwd.
     """
     q, k, v, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, lse))
     b, s, hq, hkv, d = _check(q, k, v)
+    lens = _lengths(seqlens, b, s)
     grp = hq // hkv
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     todo = heads if heads is not None else [(bb, hh) for bb in range(b) for hh in range(hq)]
     for bb, hh in todo:
-        g = hh // grp
-        S = scores(q[bb, :, hh], k[bb, :, g], scale, causal)
-        P = np.exp(S - lse[bb, hh][:, None])
-        M = attn_keep_mask(seed, p_drop, bb, head_offset + hh, s, s)
-        dq[bb, :, hh], dk_h, dv_h = _bwd_from_probs(P, M, p_drop, q[bb, :, hh], k[bb, :, g],
-                                                    v[bb, :, g], do[bb, :, hh], scale)
-        dk[bb, :, g] += dk_h
-        dv[bb, :, g] += dv_h
+        g, L = hh // grp, lens[bb]
+        if L == 0:
+            continue
+        S = scores(q[bb, :L, hh], k[bb, :L, g], scale, causal)
+        P = np.exp(S - lse[bb, hh, :L][:, None])
+        M = attn_keep_mask(seed, p_drop, bb, head_offset + hh, L, L)
+        dq[bb, :L, hh], dk_h, dv_h = _bwd_from_probs(P, M, p_drop, q[bb, :L, hh], k[bb, :L, g],
+                                                     v[bb, :L, g], do[bb, :L, hh], scale)
+        dk[bb, :L, g] += dk_h
+        dv[bb, :L, g] += dv_h
     return dq, dk, dv
 
 

@@ -201,3 +201,67 @@ def test_heads_subset_matches_full():
     Os, ls = at.attn_fwd(q, k, v, heads=[(1, 3)], **kw)
     np.testing.assert_array_equal(Os[1, :, 3], O[1, :, 3])
     np.testing.assert_array_equal(ls[1, 3], lse[1, 3])
+
+
+def _sdpa_padded(q, k, v, do, lens, causal, scale):
+    """torch SDPA (CPU, float64) with a key-padding (and causal) boolean mask;
+    dO of padded query rows is zeroed so that they contribute nothing."""
+    b, s, hq, _ = q.shape
+    grp = hq // k.shape[2]
+    allow = np.zeros((b, 1, s, s), dtype=bool)
+    for bb, L in enumerate(lens):
+        allow[bb, 0, :, :L] = True
+    if causal:
+        allow &= np.tril(np.ones((s, s), dtype=bool))[None, None]
+    allow[:, :, :, 0] |= ~allow.any(axis=3)      # rows with no visible key: any finite output, discarded
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    o = F.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(grp, 1),
+        tv.permute(0, 2, 1, 3).repeat_interleave(grp, 1), attn_mask=torch.tensor(allow), scale=scale)
+    gdo = do.copy()
+    for bb, L in enumerate(lens):
+        gdo[bb, L:] = 0.0
+    o.permute(0, 2, 1, 3).backward(torch.tensor(gdo))
+    return o.permute(0, 2, 1, 3).detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal,hq,hkv", [(True, 2, 2), (False, 4, 2), (True, 4, 1)])
+def test_padded_batch_p0_equals_masked_sdpa(causal, hq, hkv):
+    """Padded batch, p = 0: valid rows equal torch SDPA with a key-padding
+    mask (forward and autograd backward); padded rows are zero, LSE -inf."""
+    lens = [37, 0, 50, 12]
+    q, k, v, do = _inputs(4, 50, hq, hkv, 16, seed=9)
+    scale = 1 / np.sqrt(16)
+    O, lse = at.attn_fwd(q, k, v, causal=causal, scale=scale, p_drop=0.0, seed=0, seqlens=lens)
+    dq, dk, dv = at.attn_bwd(q, k, v, lse, do, causal=causal, scale=scale, p_drop=0.0, seed=0, seqlens=lens)
+    o_ref, dq_ref, dk_ref, dv_ref = _sdpa_padded(q, k, v, do, lens, causal, scale)
+    for bb, L in enumerate(lens):
+        np.testing.assert_allclose(O[bb, :L], o_ref[bb, :L], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dq[bb, :L], dq_ref[bb, :L], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk[bb], dk_ref[bb], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv[bb], dv_ref[bb], rtol=1e-10, atol=1e-12)
+        assert not O[bb, L:].any() and not dq[bb, L:].any()
+        assert not dk[bb, L:].any() and not dv[bb, L:].any()
+        assert np.all(np.isneginf(lse[bb, :, L:]))
+
+
+def test_padded_batch_with_dropout_equals_truncated_sequences():
+    """With dropout, each element of a padded batch equals the same element
+    run alone at its valid length: the mask keeps its global counters."""
+    lens = [33, 64, 1]
+    q, k, v, do = _inputs(3, 64, 2, 1, 16, seed=10)
+    kw = dict(causal=True, scale=0.25, p_drop=0.2, seed=77, head_offset=3)
+    O, lse = at.attn_fwd(q, k, v, seqlens=lens, **kw)
+    dq, dk, dv = at.attn_bwd(q, k, v, lse, do, seqlens=lens, **kw)
+    for bb, L in enumerate(lens):
+        # batch index bb enters the counters: run the element at its own index
+        sl = lambda x: x[: bb + 1, :L]
+        O1, lse1 = at.attn_fwd(sl(q), sl(k), sl(v), heads=[(bb, h) for h in range(2)], **kw)
+        dq1, dk1, dv1 = at.attn_bwd(sl(q), sl(k), sl(v), lse1, sl(do), heads=[(bb, h) for h in range(2)], **kw)
+        np.testing.assert_array_equal(O[bb, :L], O1[bb])
+        np.testing.assert_array_equal(lse[bb, :, :L], lse1[bb])
+        np.testing.assert_array_equal(dq[bb, :L], dq1[bb])
+        np.testing.assert_array_equal(dk[bb, :L], dk1[bb])
+        np.testing.assert_array_equal(dv[bb, :L], dv1[bb])
