@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SRAT_VERSION 1
+#define SRAT_VERSION 2
 
 enum srat_status {
   SRAT_OK = 0,
@@ -80,6 +80,11 @@ enum srat_norm_kind { SRAT_LAYERNORM = 1, SRAT_RMSNORM = 2 };
  * dK and dV share K's and V's.  Strides and base pointers must be multiples of
  * 8 elements (16 bytes) for bf16 and of 4 elements for fp32.
  * Grouped-query attention: q-head hh reads kv-head hh / (hq / hkv).
+ * Padded batches: with seqlens != NULL, batch element bb acts on its first
+ * L = seqlens[bb] positions only, as if its sequence had length L: keys at or
+ * past L are invisible, the dropout mask keeps its global counters, and the
+ * padded positions get O = 0, LSE = -inf and dQ = dK = dV = 0.  Lengths are
+ * read on the device and clamped to [0, s].  bf16 path only.
  */
 typedef struct {
   int32_t dtype;          /* SRAT_BF16 (MFMA path) or SRAT_F32 (reference-precision path) */
@@ -93,6 +98,7 @@ typedef struct {
   float p_drop;           /* attention-dropout probability in [0, 1); 0 disables it */
   uint64_t seed;          /* Philox key of the attention dropout */
   int64_t head_offset;    /* global index of local q-head 0 (TP rank * hq) */
+  const int32_t* seqlens; /* NULL, or device pointer to b valid lengths (int32, 4-byte aligned) */
 } srat_attn_desc;
 
 /*

@@ -78,6 +78,9 @@ int check_attn(const srat_attn_desc* d) {
     return fail(SRAT_ERR_INVALID, "head_offset out of range");
   if (!(d->p_drop >= 0.f && d->p_drop < 1.f)) return fail(SRAT_ERR_INVALID, "p_drop %g not in [0, 1)", d->p_drop);
   if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return fail(SRAT_ERR_INVALID, "scale must be finite and > 0");
+  if (d->seqlens && d->dtype != SRAT_BF16)
+    return fail(SRAT_ERR_UNSUPPORTED, "per-element sequence lengths need the bf16 path");
+  if (d->seqlens && !aligned(d->seqlens, 4)) return fail(SRAT_ERR_INVALID, "seqlens must be 4-byte aligned");
   const int64_t al = d->dtype == SRAT_BF16 ? 8 : 4;
   const int64_t* st[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
   for (int t = 0; t < 4; ++t)
@@ -109,6 +112,7 @@ srat::AttnParams attn_params(const srat_attn_desc* d) {
   p.k0 = (uint32_t)(d->seed & 0xFFFFFFFFu);
   p.k1 = (uint32_t)(d->seed >> 32);
   p.head_offset = (int32_t)d->head_offset;
+  p.seqlens = d->seqlens;
   return p;
 }
 

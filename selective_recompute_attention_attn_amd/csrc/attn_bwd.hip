@@ -122,7 +122,9 @@ using bool_c = std::integral_constant<bool, B>;
 template <int D, bool CAUSAL>
 constexpr bool kSplitBwd = CAUSAL && D >= 128;
 
-template <int D, bool CAUSAL, bool DROP, bool PART>
+// VARLEN: per-element valid lengths (padded batch); compiled separately so
+// that the plain kernels keep their code.
+template <int D, bool CAUSAL, bool DROP, bool PART, bool VARLEN>
 __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) void attn_bwd_dkdv_kernel(AttnParams p) {
   constexpr int QH = DkdvCfg<D>::kQH;
   constexpr bool kVLds = DkdvCfg<D>::kVLds;
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   const int half = lane >> 5, col = lane & 31;
   const int k0 = kblk * kBNk;
   const int kw0 = k0 + 32 * kg;                       // first key of this wave
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;      // valid length of this batch element
 
   const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
   const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   bf16x8 kreg[kDC], vreg[kVLds ? 1 : kDC];
   {
     const int key = kw0 + perm32(col);
-    const bool ok = key < p.s;
+    const bool ok = key < sl;
     const int64_t ko = (int64_t)(ok ? key : 0) * p.sk_s + 8 * half;
     const int64_t vo = (int64_t)(ok ? key : 0) * p.sv_s + 8 * half;
 #pragma unroll
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     // the block's 128 V rows -> LDS in slot order (rows past s read as zero);
     // made visible by the first tile's barrier
     constexpr int kVS = SM::kVS;
-    const int rows = min(kBNk, p.s - k0);
+    const int rows = max(0, min(kBNk, sl - k0));
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + (int64_t)k0 * p.sv_s, (uint32_t)((int64_t)rows * p.sv_s * 2));
 #pragma unroll
     for (int it = 0; it < kBNk * D / 8 / kThreads; ++it) {
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
 #pragma unroll
   for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
 
-  const int nqt_all = (p.s + kRows - 1) / kRows;
+  const int nqt_all = (sl + kRows - 1) / kRows;
   const int qt_first = CAUSAL ? k0 / kRows : 0;
   // query tiles [qt0, nqt) of this workgroup
   const int qt_mid = qt_first + (nqt_all - qt_first + 1) / 2;
@@ -230,12 +233,12 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     ooff[it] = in ? (uint32_t)(((int64_t)(x / (D / 8)) * p.so_s + 8 * (x % (D / 8))) * 2) : 0xFFFFFFF0u;
   }
   auto tile_bytes = [&](int qt, int64_t stride) -> uint32_t {
-    const int rows = min(kRows, max(0, p.s - qt * kRows));
+    const int rows = min(kRows, max(0, sl - qt * kRows));
     return (uint32_t)((int64_t)rows * stride * 2);
   };
   // per-row LSE / D of the lane's query (zero past s), fetched one tile ahead
-  const __amdgpu_buffer_rsrc_t rlse = buffer_rsrc(p.lse + row0, (uint32_t)p.s * 4u);
-  const __amdgpu_buffer_rsrc_t rdel = buffer_rsrc(p.delta + row0, (uint32_t)p.s * 4u);
+  const __amdgpu_buffer_rsrc_t rlse = buffer_rsrc(p.lse + row0, (uint32_t)sl * 4u);
+  const __amdgpu_buffer_rsrc_t rdel = buffer_rsrc(p.delta + row0, (uint32_t)sl * 4u);
   float lse_n = 0.f, dlt_n = 0.f;
   auto load_rowstats = [&](int qt) {
     const int qo = (qt * kRows + 32 * qh + col) * 4;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     }
     // keys at or past kl are masked for this lane's query (all of them for a
     // query past s)
-    const int kl = qi < p.s ? (CAUSAL ? min(p.s, qi + 1) : p.s) : 0;
+    const int kl = qi < sl ? (CAUSAL ? min(sl, qi + 1) : sl) : 0;
 
     // recompute P, regenerate the mask, P*M and dS packed to bf16 pairs
     uint32_t pmw[8], dsw[8];
@@ -365,28 +368,31 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     }
   };
 
-  // prologue: Q/dO[qt0] resident, Q/dO[qt0+1] and the row stats of qt0 in flight
-  load_tile(qt0);
-  stash(0);
-  load_rowstats(qt0);
-  load_tile(qt0 + 1);
-  // Tiles this wave computes without masking: every query of the tile at or
-  // past every key of the wave (causal) and everything inside s.
-  const int last = nqt - 1;
-  int qa = qt0, qb = qt0;
-  if (kw0 + 32 <= p.s) {
-    qa = CAUSAL ? max(qt0, (kw0 + 31 - 32 * qh + kRows - 1) / kRows) : qt0;   // first q0 >= kw0 + 31
-    qb = max(qa, (p.s - 32 * qh - 32) / kRows + 1);                            // last q0 + 31 < s
-    qb = min(qb, nqt);
-    if ((p.s - 32 * qh - 32) < 0) qb = qa;
+  // a key block past the valid length (padded batch) keeps dK = dV = 0
+  if (!VARLEN || k0 < sl) {
+    // prologue: Q/dO[qt0] resident, Q/dO[qt0+1] and the row stats of qt0 in flight
+    load_tile(qt0);
+    stash(0);
+    load_rowstats(qt0);
+    load_tile(qt0 + 1);
+    // Tiles this wave computes without masking: every query of the tile at or
+    // past every key of the wave (causal) and everything inside sl.
+    const int last = nqt - 1;
+    int qa = qt0, qb = qt0;
+    if (kw0 + 32 <= sl) {
+      qa = CAUSAL ? max(qt0, (kw0 + 31 - 32 * qh + kRows - 1) / kRows) : qt0;   // first q0 >= kw0 + 31
+      qb = max(qa, (sl - 32 * qh - 32) / kRows + 1);                             // last q0 + 31 < sl
+      qb = min(qb, nqt);
+      if ((sl - 32 * qh - 32) < 0) qb = qa;
+    }
+    // separate straight-line loops (see the forward kernel)
+    int qt = qt0;
+    for (; qt < min(qa, last); ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
+    for (; qt < min(qb, last); ++qt) tile(qt, bool_c<false>{}, bool_c<true>{});
+    for (; qt < last; ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
+    if (qt >= qa && qt < qb) tile(qt, bool_c<false>{}, bool_c<false>{});
+    else tile(qt, bool_c<true>{}, bool_c<false>{});
   }
-  // separate straight-line loops (see the forward kernel)
-  int qt = qt0;
-  for (; qt < min(qa, last); ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
-  for (; qt < min(qb, last); ++qt) tile(qt, bool_c<false>{}, bool_c<true>{});
-  for (; qt < last; ++qt) tile(qt, bool_c<true>{}, bool_c<true>{});
-  if (qt >= qa && qt < qb) tile(qt, bool_c<false>{}, bool_c<false>{});
-  else tile(qt, bool_c<true>{}, bool_c<false>{});
 
   // two query halves: the second adds its share into the first through LDS
   if (QH == 2) {
@@ -458,7 +464,7 @@ __device__ __forceinline__ int causal_tile(int rank, int nqt) {
 
 template <int D> struct DqOcc { static constexpr int kWavesPerEU = D <= 96 ? 2 : 1; };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel(AttnParams p) {
   constexpr int kKS = DqSmem<D>::kKS;
   constexpr int kVS = DqSmem<D>::kVS;
@@ -490,6 +496,8 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int qw = q0 + 32 * wv;
   const int qi = qw + col;
   const bool qvalid = qi < p.s;
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;   // valid length of this batch element
+  const bool qlive = VARLEN ? qi < sl : qvalid;      // a query row inside it
 
   const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
   const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
@@ -501,20 +509,20 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   bf16x8 qreg[kDC], doreg[kDC];
 #pragma unroll
   for (int c = 0; c < kDC; ++c) qreg[c] = doreg[c] = bf16x8{};
-  if (qvalid) {
+  if (qlive) {
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
       qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
       doreg[c] = *reinterpret_cast<const bf16x8*>(dop + (int64_t)qi * p.so_s + 16 * c + 8 * half);
     }
   }
-  // rows past s compute garbage that only reaches their own (unstored) dQ rows
-  const float lse2 = qvalid ? p.lse[row0 + qi] * kLog2e : 0.f;
+  // rows past the valid length see no key (dQ = 0, D = 0); rows past s are not stored
+  const float lse2 = qlive ? p.lse[row0 + qi] * kLog2e : 0.f;
   // D = rowsum(dO * O) of the lane's query: the lane's d-slices of O against
   // the same slices of dO (doreg), plus the other lane half's complementary
   // slices; stored for the dK/dV kernel, which runs after this one
   float dlt = 0.f;
-  if (qvalid) {
+  if (qlive) {
     const bf16* orow = static_cast<const bf16*>(p.o) + bb * p.so_b + hh_q * p.so_h + (int64_t)qi * p.so_s;
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
@@ -530,14 +538,15 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
 #pragma unroll
   for (int db = 0; db < kDB; ++db) qacc[db] = f32x16{};
 
-  const int nkt_all = (p.s + kQN - 1) / kQN;
+  const int nkt_all = (sl + kQN - 1) / kQN;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + kQM + kQN - 1) / kQN) : nkt_all;
-  const int n_int = CAUSAL ? min(p.s / kQN, (qw + 1) / kQN) : p.s / kQN;
+  // tiles this wave computes without masking (none if it holds a row past sl)
+  const int n_int = (VARLEN && qw + 31 >= sl) ? 0 : CAUSAL ? min(sl / kQN, (qw + 1) / kQN) : sl / kQN;
   // key tiles [kt_lo, kt_hi) of this workgroup
   const int kt_mid = (nkt + 1) / 2;
   const int kt_lo = part == 1 ? kt_mid : 0;
   const int kt_hi = part == 0 ? kt_mid : nkt;
-  const int key_lim = CAUSAL ? min(p.s, qi + 1) : p.s;
+  const int key_lim = VARLEN ? (qlive ? (CAUSAL ? min(sl, qi + 1) : sl) : 0) : (CAUSAL ? min(p.s, qi + 1) : p.s);
 
   // ---- K/V staging through buffer loads (keys past s read as zero)
   uint4 kpre[kLoads], vpre[kLoads];
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
   }
   auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
-    const int rows = min(kQN, max(0, p.s - kt * kQN));
+    const int rows = min(kQN, max(0, sl - kt * kQN));
     return (uint32_t)((int64_t)rows * stride * 2);
   };
   auto load_kv = [&](int kt) {
@@ -660,6 +669,8 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
     }
   };
 
+  // a query tile past the valid length (padded batch) sees no key (key_lim
+  // is 0 for all its rows): its tiles leave dQ = 0
   // prologue: K/V[kt_lo] resident, K/V[kt_lo+1] in flight
   load_kv(kt_lo);
   stash_kv(kt_lo & 1);
@@ -670,6 +681,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   for (; kt < kt_hi - 1; ++kt) tile(kt, bool_c<true>{}, bool_c<true>{});
   if (kt < n_int) tile(kt, bool_c<false>{}, bool_c<false>{});
   else tile(kt, bool_c<true>{}, bool_c<false>{});
+
 
   // a split tile's part: the raw fp32 dQ^T partial, [2][b, hq, s, d]
   if (part >= 0) {
@@ -765,14 +777,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_sum_kernel(AttnParams p, int 
   *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool VARLEN>
 hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   const bool part = p.hq != p.hkv;
   const unsigned nbh = (unsigned)(p.hq * p.b);
   {
     TraceScope ts("attn_bwd_dq", st);
     const unsigned nqt = (unsigned)((p.s + kQM - 1) / kQM);
-    attn_bwd_dq_kernel<D, CAUSAL, DROP><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
+    attn_bwd_dq_kernel<D, CAUSAL, DROP, VARLEN><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -789,8 +801,8 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
     const unsigned nkb = (unsigned)((p.s + kBNk - 1) / kBNk);
     const dim3 grid((nkb + p.split_kb) * nbh);
     const int threads = 256 * DkdvCfg<D>::kQH;
-    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true><<<grid, threads, 0, st>>>(p);
-    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false><<<grid, threads, 0, st>>>(p);
+    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, threads, 0, st>>>(p);
+    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, threads, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -802,11 +814,16 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, bool VARLEN>
+hipError_t bwd_launch_v(const AttnParams& p, hipStream_t st) {
+  const bool drop = p.thresh != 0;
+  if (p.causal) return drop ? bwd_main<D, true, true, VARLEN>(p, st) : bwd_main<D, true, false, VARLEN>(p, st);
+  return drop ? bwd_main<D, false, true, VARLEN>(p, st) : bwd_main<D, false, false, VARLEN>(p, st);
+}
+
 template <int D>
 hipError_t bwd_launch_d(const AttnParams& p, hipStream_t st) {
-  const bool drop = p.thresh != 0;
-  if (p.causal) return drop ? bwd_main<D, true, true>(p, st) : bwd_main<D, true, false>(p, st);
-  return drop ? bwd_main<D, false, true>(p, st) : bwd_main<D, false, false>(p, st);
+  return p.seqlens ? bwd_launch_v<D, true>(p, st) : bwd_launch_v<D, false>(p, st);
 }
 
 }  // namespace

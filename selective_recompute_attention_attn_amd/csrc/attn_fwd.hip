@@ -89,7 +89,9 @@ constexpr bool kSplitFwd = CAUSAL && fwd_occupancy<D>() == 1;
 //   issue the MFMAs of S[t+1] = K[t+1] Q^T   || exp / row sum / dropout of S[t]
 //   issue the MFMAs of O^T += V[t]^T P[t]^T  || Philox draws for tile t+1
 // so the matrix cores and the vector ALUs of a wave work on different tiles.
-template <int D, bool CAUSAL, bool DROP>
+// VARLEN: per-element valid lengths (padded batch); compiled separately so
+// that the plain kernels keep their code.
+template <int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_kernel(AttnParams p) {
   constexpr int kKS = FwdSmem<D>::kKS;
   constexpr int kVS = FwdSmem<D>::kVS;
@@ -122,16 +124,39 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   const int q0 = qt * kBM;
   const int qw = q0 + 32 * wv;           // first query of this wave
   const int qi = qw + col;               // this lane's query
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;   // valid length of this batch element
 
   const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
   const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
   const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
 
+  // a tile past the valid length (padded batch): O = 0, LSE = -inf (a split
+  // tile's parts: O / l = 0, LSE = -inf, which the merge turns into the same)
+  if (VARLEN && q0 >= sl) {
+    if (qi < p.s) {
+      const int64_t row = ((int64_t)bb * p.hq + hh_q) * p.s + qi;
+      if (part >= 0) {
+        const int64_t prow = (int64_t)part * p.b * p.hq * p.s + row;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j)
+          if (j % 2 == half) *reinterpret_cast<float4*>(p.o_part + prow * D + 4 * j) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (half == 0) p.lse_part[prow] = -INFINITY;
+      } else {
+        bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c)
+          if (c % 2 == half) *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(0, 0, 0, 0);
+        if (half == 0) p.lse_out[row] = -INFINITY;
+      }
+    }
+    return;
+  }
+
   // Q^T B operand: lane (col, half) holds Q[qi][16c + 8*half .. +7]
   bf16x8 qreg[kDC];
 #pragma unroll
   for (int c = 0; c < kDC; ++c) qreg[c] = bf16x8{};
-  if (qi < p.s) {
+  if (qi < sl) {
 #pragma unroll
     for (int c = 0; c < kDC; ++c)
       qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
@@ -143,16 +168,16 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   float m_use = -INFINITY;   // running max, log2-scaled units
   float l_run = 0.f;         // lane-partial row sum (this lane's keys)
 
-  const int nkt_all = (p.s + kBN - 1) / kBN;
+  const int nkt_all = (sl + kBN - 1) / kBN;
   const int nkt_q = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
   // key tiles [kt_lo, nkt) of this workgroup
   const int kt_mid = (nkt_q + 1) / 2;
   const int kt_lo = part == 1 ? kt_mid : 0;
   const int nkt = part == 0 ? kt_mid : nkt_q;
   // tiles 0 .. n_int-1 need no masking for any query of this wave
-  const int n_int = CAUSAL ? min(p.s / kBN, (qw + 1) / kBN) : p.s / kBN;
+  const int n_int = CAUSAL ? min(sl / kBN, (qw + 1) / kBN) : sl / kBN;
   // keys at or beyond key_lim are masked for this lane's query
-  const int key_lim = CAUSAL ? min(p.s, qi + 1) : p.s;
+  const int key_lim = CAUSAL ? min(sl, qi + 1) : sl;
 
   // ---- global <-> LDS staging; chunk x = tid + 256*it of a 64 x D tile.
   // Buffer loads: the tile's base and its valid byte count are scalars, keys
@@ -166,7 +191,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
   }
   auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
-    const int rows = min(kBN, max(0, p.s - kt * kBN));
+    const int rows = min(kBN, max(0, sl - kt * kBN));
     return (uint32_t)((int64_t)rows * stride * 2);
   };
   auto load_k = [&](int kt) {
@@ -360,7 +385,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
       const int64_t row = (int64_t)part * p.b * p.hq * p.s + ((int64_t)bb * p.hq + hh_q) * p.s + qi;
       // a row can have no visible key in one part (the first tile's early
       // rows in part 1): O = 0 and LSE = -inf give it zero weight in the merge
-      const bool any = l_tot > 0.f;
+      const bool any = l_tot > 0.f && (!VARLEN || qi < sl);
       const float inv = any ? 1.0f / l_tot : 0.f;
       float* dst = p.o_part + row * D;
 #pragma unroll
@@ -375,7 +400,8 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     return;
   }
   if (qi < p.s) {
-    const float inv = p.inv_keep / l_tot;
+    const bool valid = !VARLEN || qi < sl;   // rows past the valid length: O = 0, LSE = -inf
+    const float inv = valid ? p.inv_keep / l_tot : 0.f;
     bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
@@ -387,7 +413,8 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
         *reinterpret_cast<uint2*>(op + 32 * db + 8 * a + 4 * half) = w;
       }
     }
-    if (half == 0) p.lse_out[((int64_t)bb * p.hq + hh_q) * p.s + qi] = (m_use + __log2f(l_tot)) * kLn2;
+    if (half == 0)
+      p.lse_out[((int64_t)bb * p.hq + hh_q) * p.s + qi] = valid ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -408,8 +435,10 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnParams p, int q
   const int64_t part_rows = (int64_t)p.b * p.hq * p.s;
   const float l0 = p.lse_part[row], l1 = p.lse_part[part_rows + row];
   const float mx = fmaxf(l0, l1);
-  const float lse = mx + log1pf(__expf(fminf(l0, l1) - mx));
-  const float w0 = __expf(l0 - lse) * p.inv_keep, w1 = __expf(l1 - lse) * p.inv_keep;
+  const bool none = mx == -INFINITY;     // a padded row: no visible key in either part
+  const float lse = none ? -INFINITY : mx + log1pf(__expf(fminf(l0, l1) - mx));
+  const float w0 = none ? 0.f : __expf(l0 - lse) * p.inv_keep;
+  const float w1 = none ? 0.f : __expf(l1 - lse) * p.inv_keep;
   const float* s0 = p.o_part + row * D + 8 * c8;
   const float* s1 = s0 + part_rows * D;
   const float4 a0 = reinterpret_cast<const float4*>(s0)[0], b0 = reinterpret_cast<const float4*>(s0)[1];
@@ -424,19 +453,19 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnParams p, int q
   if (c8 == 0) p.lse_out[row] = lse;
 }
 
-template <int D>
-hipError_t fwd_launch_d(const AttnParams& p, hipStream_t st) {
+template <int D, bool VARLEN>
+hipError_t fwd_launch_v(const AttnParams& p, hipStream_t st) {
   const int nqt = (p.s + kBM - 1) / kBM;
   const dim3 grid((unsigned)((nqt + p.split_qt) * p.hq * p.b));
   const bool drop = p.thresh != 0;
   {
     TraceScope ts("attn_fwd_bf16", st);
     if (p.causal) {
-      if (drop) attn_fwd_bf16_kernel<D, true, true><<<grid, kThreads, 0, st>>>(p);
-      else attn_fwd_bf16_kernel<D, true, false><<<grid, kThreads, 0, st>>>(p);
+      if (drop) attn_fwd_bf16_kernel<D, true, true, VARLEN><<<grid, kThreads, 0, st>>>(p);
+      else attn_fwd_bf16_kernel<D, true, false, VARLEN><<<grid, kThreads, 0, st>>>(p);
     } else {
-      if (drop) attn_fwd_bf16_kernel<D, false, true><<<grid, kThreads, 0, st>>>(p);
-      else attn_fwd_bf16_kernel<D, false, false><<<grid, kThreads, 0, st>>>(p);
+      if (drop) attn_fwd_bf16_kernel<D, false, true, VARLEN><<<grid, kThreads, 0, st>>>(p);
+      else attn_fwd_bf16_kernel<D, false, false, VARLEN><<<grid, kThreads, 0, st>>>(p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_qt == 0) return e;
@@ -446,6 +475,11 @@ hipError_t fwd_launch_d(const AttnParams& p, hipStream_t st) {
   const int64_t n = (int64_t)p.b * p.hq * (p.s - q_lo) * (D / 8);
   attn_fwd_merge_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, q_lo);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t fwd_launch_d(const AttnParams& p, hipStream_t st) {
+  return p.seqlens ? fwd_launch_v<D, true>(p, st) : fwd_launch_v<D, false>(p, st);
 }
 
 __global__ void attn_mask_kernel(AttnParams p, uint8_t* mask) {

@@ -82,6 +82,7 @@ struct AttnParams {
   uint32_t thresh;     // 16-bit drop threshold, 0 = no dropout
   uint32_t k0, k1;
   int32_t head_offset;
+  const int32_t* seqlens;  // [b] valid lengths of a padded batch, or null (all s)
   int32_t split_qt;    // 128-query tiles whose keys are split over two workgroups (forward, dQ)
   int32_t split_kb;    // backward: 128-key blocks whose queries are split over two dK/dV workgroups
 };
@@ -97,6 +98,13 @@ struct AttnSplit {
   int32_t split_kb;
 };
 AttnSplit attn_grid_split(int64_t b, int64_t s, int64_t hq, int64_t d, bool causal, bool bf16);
+
+// Valid length of batch element bb: seqlens[bb] clamped to [0, s], or s.
+// Wave-uniform (bb is), read through the scalar cache.
+__device__ __forceinline__ int attn_len(const AttnParams& p, int bb) {
+  if (!p.seqlens) return p.s;
+  return min(max(p.seqlens[bb], 0), p.s);
+}
 
 hipError_t launch_attn_fwd(const AttnParams& p, bool bf16, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnParams& p, bool bf16, hipStream_t st);

@@ -33,7 +33,7 @@ class AttnDesc(ctypes.Structure):
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
                 ("scale", ctypes.c_float), ("p_drop", ctypes.c_float),
-                ("seed", ctypes.c_uint64), ("head_offset", ctypes.c_int64)]
+                ("seed", ctypes.c_uint64), ("head_offset", ctypes.c_int64), ("seqlens", ctypes.c_void_p)]
 
 
 class NormDesc(ctypes.Structure):
@@ -110,8 +110,17 @@ def _strides(t: torch.Tensor):
     return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
+def _seqlens_ptr(seqlens: torch.Tensor, b: int, device) -> int:
+    if seqlens.dtype != torch.int32 or seqlens.shape != (b,) or not seqlens.is_contiguous() \
+            or seqlens.device != device:
+        raise SratError("seqlens must be a contiguous int32 [b] tensor on the tensors' device")
+    return seqlens.data_ptr()
+
+
 def attn_desc(q, k, v, o, *, causal: bool, scale: Optional[float], p_drop: float, seed: int,
-              head_offset: int) -> AttnDesc:
+              head_offset: int, seqlens: Optional[torch.Tensor] = None) -> AttnDesc:
+    """Descriptor of one attention problem.  seqlens: optional int32 [b] device
+    tensor of valid lengths (padded batch)."""
     b, s, hq, d = q.shape
     hkv = k.shape[2]
     if k.shape != (b, s, hkv, d) or v.shape != k.shape or o.shape != q.shape:
@@ -121,7 +130,8 @@ def attn_desc(q, k, v, o, *, causal: bool, scale: Optional[float], p_drop: float
     return AttnDesc(dtype=_dtype_code(q), causal=int(bool(causal)), b=b, s=s, hq=hq, hkv=hkv, d=d,
                     q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o),
                     scale=float(1.0 / math.sqrt(d) if scale is None else scale), p_drop=float(p_drop),
-                    seed=int(seed) & 0xFFFFFFFFFFFFFFFF, head_offset=int(head_offset))
+                    seed=int(seed) & 0xFFFFFFFFFFFFFFFF, head_offset=int(head_offset),
+                    seqlens=None if seqlens is None else _seqlens_ptr(seqlens, b, q.device))
 
 
 class Call:
@@ -159,27 +169,30 @@ def attn_fwd_workspace_bytes(desc: AttnDesc) -> int:
 
 def prepare_attn_fwd(q, k, v, o, lse, *, causal: bool = False, scale: Optional[float] = None,
                      p_drop: float = 0.0, seed: int = 0, head_offset: int = 0, workspace=None,
-                     stream=None) -> Call:
+                     seqlens: Optional[torch.Tensor] = None, stream=None) -> Call:
     """srat_attn_core_fwd_ws on fixed buffers (o, lse preallocated; workspace of
     attn_fwd_workspace_bytes or None); stream defaults to torch's current stream
     at preparation time."""
     b, s, hq, d = q.shape
     if lse.shape != (b, hq, s) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise SratError("lse must be a contiguous float32 [b, hq, s] tensor")
-    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset,
+                     seqlens=seqlens)
     ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), ws_ptr, ws_bytes,
             _stream_arg(q.device, stream))
-    return Call("srat_attn_core_fwd_ws", args, (desc, q, k, v, o, lse, workspace))
+    return Call("srat_attn_core_fwd_ws", args, (desc, q, k, v, o, lse, workspace, seqlens))
 
 
 def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
                   scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  workspace: Optional[torch.Tensor] = None, seqlens: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
     """O = dropout(softmax(q k^T * scale)) v and the per-row LSE [b, hq, s] (fp32).
 
     workspace: None allocates the one the shape can use (none for most shapes).
+    seqlens: optional int32 [b] device tensor of valid lengths (padded batch).
     """
     b, s, hq, d = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
@@ -189,7 +202,7 @@ def attn_core_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: 
                                                   seed=seed, head_offset=head_offset))
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     prepare_attn_fwd(q, k, v, o, l, causal=causal, scale=scale, p_drop=p_drop, seed=seed,
-                     head_offset=head_offset, workspace=workspace)()
+                     head_offset=head_offset, workspace=workspace, seqlens=seqlens)()
     return o, l
 
 
@@ -202,26 +215,28 @@ def attn_bwd_workspace_bytes(desc: AttnDesc) -> int:
 
 def prepare_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, *, causal: bool = False,
                      scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
-                     stream=None) -> Call:
+                     seqlens: Optional[torch.Tensor] = None, stream=None) -> Call:
     """srat_attn_core_bwd on fixed buffers: gradients (with the strides of q, k, v)
     and the workspace (attn_bwd_workspace_bytes) preallocated."""
     if dout.shape != o.shape or dout.stride() != o.stride():
         raise SratError("dout must have o's shape and strides")
-    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset)
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset,
+                     seqlens=seqlens)
     for t, ref in ((dq, q), (dk, k), (dv, v)):
         if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
             raise SratError("preallocated gradients must match q, k, v")
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel(), _stream_arg(q.device, stream))
-    return Call("srat_attn_core_bwd", args, (desc, q, k, v, o, lse, dout, dq, dk, dv, workspace))
+    return Call("srat_attn_core_bwd", args, (desc, q, k, v, o, lse, dout, dq, dk, dv, workspace, seqlens))
 
 
 def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
                   p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
-                  workspace: Optional[torch.Tensor] = None, outs=None):
+                  workspace: Optional[torch.Tensor] = None, outs=None, seqlens: Optional[torch.Tensor] = None):
     """dq, dk, dv by recomputation of scores, softmax and dropout mask.
 
     outs: optional preallocated (dq, dk, dv) with the strides of (q, k, v).
+    seqlens: the forward's valid lengths (padded batch), or None.
     """
     if outs is None:
         dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
@@ -234,7 +249,7 @@ def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optiona
                          head_offset=head_offset)
         workspace = torch.empty(max(attn_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=q.device)
     prepare_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=causal, scale=scale, p_drop=p_drop,
-                     seed=seed, head_offset=head_offset)()
+                     seed=seed, head_offset=head_offset, seqlens=seqlens)()
     return dq, dk, dv
 
 

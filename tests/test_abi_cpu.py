@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops.EXPORTS)
-    assert L.srat_version() == 1
+    assert L.srat_version() == 2
 
 
 def _desc(**kw):
@@ -172,3 +172,15 @@ def test_threshold_rule_matches_oracle():
     for p in (0.0, 0.1, 0.25, 0.3333, 0.9999):
         t = int(float(np.float32(p)) * 65536.0 + 0.5)
         assert t == ph.drop_threshold(p)
+
+
+def test_seqlens_only_on_the_bf16_path(L):
+    """Per-element lengths are a bf16-path feature: the fp32 path refuses them
+    and a misaligned pointer is invalid, both before any HIP call."""
+    n = ctypes.c_size_t(0)
+    d = _desc(dtype=ops.SRAT_F32, seqlens=0x1000)
+    assert _err(L, L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)))[0] == -2
+    d = _desc(seqlens=0x1002)
+    assert _err(L, L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)))[0] == -1
+    d = _desc(seqlens=0x1000)
+    assert L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0

@@ -279,3 +279,67 @@ def test_forward_split_grid_and_unsplit_agree_with_the_oracle():
     assert_close("o unsplit", host(o1), o_ref, TOL_BF16)
     assert_close("o split", host(o2), o_ref, TOL_BF16)
     np.testing.assert_allclose(host(l2), host(l1), rtol=1e-5, atol=1e-5)
+
+
+PADDED = [
+    # b, s, hq, hkv, d, causal, p, valid lengths
+    (4, 200, 2, 2, 64, True, 0.1, [200, 0, 77, 129]),
+    (3, 300, 4, 2, 128, True, 0.1, [1, 300, 150]),
+    (2, 257, 3, 3, 96, False, 0.2, [256, 33]),
+    (2, 384, 2, 1, 160, True, 0.0, [383, 64]),
+    (4, 2048, 8, 8, 96, True, 0.1, [2048, 1500, 700, 31]),
+]
+
+
+@pytest.mark.parametrize("b,s,hq,hkv,d,causal,p,lens", PADDED)
+def test_padded_batch(b, s, hq, hkv, d, causal, p, lens):
+    """Per-element valid lengths: O, LSE and the gradients match the oracle's
+    padded-batch definition; padded positions are exactly O = 0, LSE = -inf,
+    dQ = dK = dV = 0."""
+    device = need_gpu()
+    a = gen.AttnShape(b=b, s=s, hq=hq, hkv=hkv, d=d, causal=causal, p_drop=p, seed=99, head_offset=1)
+    announce(f"padded batch {a} lens={lens}")
+    x = gen.attn_inputs(a, seed_base=31)
+    q, k, v, do = (dev(x[n], "bf16", device) for n in ("q", "k", "v", "do"))
+    sl = torch.tensor(lens, dtype=torch.int32, device=device)
+    kw = dict(causal=causal, scale=a.scale, p_drop=p, seed=a.seed, head_offset=a.head_offset)
+    o, lse = ops.attn_core_fwd(q, k, v, seqlens=sl, **kw)
+    dq, dk, dv = ops.attn_core_bwd(q, k, v, o, lse, do, seqlens=sl, **kw)
+    torch.cuda.synchronize()
+    heads = None if s <= 512 else [(0, 0), (1, 3), (2, 5), (3, 7)]
+    o_r, lse_r = oat.attn_fwd(x["q"], x["k"], x["v"], heads=heads, seqlens=lens, **kw)
+    dq_r, dk_r, dv_r = oat.attn_bwd(x["q"], x["k"], x["v"], lse_r, x["do"], heads=heads, seqlens=lens, **kw)
+    got = {"o": host(o), "lse": host(lse), "dq": host(dq), "dk": host(dk), "dv": host(dv)}
+    pairs = heads or [(bb, hh) for bb in range(b) for hh in range(hq)]
+    grp = hq // hkv
+    for bb, hh in pairs:
+        L = lens[bb]
+        g = hh // grp
+        assert np.all(np.isneginf(got["lse"][bb, hh, L:]))
+        assert not got["o"][bb, L:, hh].any() and not got["dq"][bb, L:, hh].any()
+        assert not got["dk"][bb, L:, g].any() and not got["dv"][bb, L:, g].any()
+        if L == 0:
+            continue
+        assert_close("lse", got["lse"][bb, hh, :L], lse_r[bb, hh, :L], TOL_BF16)
+        assert_close("o", got["o"][bb, :L, hh], o_r[bb, :L, hh], TOL_BF16)
+        assert_close("dq", got["dq"][bb, :L, hh], dq_r[bb, :L, hh], TOL_BF16)
+        if heads is None or grp == 1:
+            assert_close("dk", got["dk"][bb, :L, g], dk_r[bb, :L, g], TOL_BF16)
+            assert_close("dv", got["dv"][bb, :L, g], dv_r[bb, :L, g], TOL_BF16)
+
+
+def test_full_lengths_equal_no_lengths():
+    """seqlens all equal to s gives the unpadded results bit for bit."""
+    device = need_gpu()
+    a = gen.AttnShape(b=2, s=320, hq=4, hkv=2, d=128, causal=True, p_drop=0.1, seed=5)
+    announce("full lengths")
+    x = gen.attn_inputs(a)
+    ref = run_gpu(a, x, device)
+    q, k, v, do = (dev(x[n], "bf16", device) for n in ("q", "k", "v", "do"))
+    sl = torch.full((a.b,), a.s, dtype=torch.int32, device=device)
+    kw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed, head_offset=a.head_offset)
+    o, lse = ops.attn_core_fwd(q, k, v, seqlens=sl, **kw)
+    dq, dk, dv = ops.attn_core_bwd(q, k, v, o, lse, do, seqlens=sl, **kw)
+    torch.cuda.synchronize()
+    for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_array_equal(host(t), ref[n])
