@@ -34,8 +34,10 @@
 //         (the most queries) are launched first; where two workgroups share
 //         a CU, the grid's second half runs in the mirrored order so that
 //         each pair carries about the same work.
-//   gqa_sum: grouped-query attention only: dK, dV = sums over the q-heads that
-//         share a kv-head of the per-q-head fp32 partials.
+//   kv_sum: grouped-query attention or split key blocks: dK, dV = sums, in a
+//         fixed order, of the fp32 partials of the q-heads that share a
+//         kv-head and of the two halves of a split block.
+//   dq_sum: split query tiles: dQ = the sum of the two halves' fp32 partials.
 #include <algorithm>
 #include <type_traits>
 
