@@ -473,6 +473,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kLoads = D / 32;
+  constexpr bool kPreK = DqOcc<D>::kWavesPerEU == 1;   // K^T operands read one phase early
   __shared__ DqSmem<D> sm;
 
   const int nqt = (p.s + kQM - 1) / kQM;
@@ -594,6 +595,14 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   const int grp = lane >> 4, lg = lane & 15;
   const int ktr = (4 * (grp >> 1) + (lg >> 2)) * kKS + 16 * (grp & 1) + 4 * (lg & 3);
 
+  // K^T A operand of dQ step c (keys 32(c/2) + 16(c%2) ..), d block db, from
+  // a row-major K tile through two transposing reads
+  auto kt_operand = [&](const bf16* kb_, int c, int db) -> bf16x8 {
+    const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kKS + ktr;
+    const s16x4 lo = lds_read_tr16(&kb_[r0 + 32 * db]);
+    const s16x4 hi = lds_read_tr16(&kb_[r0 + 8 * kKS + 32 * db]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto tile = [&](int kt, auto mask_c, auto next_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
@@ -621,6 +630,15 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
         sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * kb * kKS + kro + 16 * c]), qreg[c], sacc[kb]);
         pacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.v[buf][32 * kb * kVS + vro + 16 * c]), doreg[c], pacc[kb]);
       }
+    // with one wave per SIMD nothing else hides the LDS latency of the K^T
+    // operands of dQ, so they are read here, behind the MFMAs above
+    bf16x8 kop[kPreK ? 4 : 1][kPreK ? kDB : 1];
+    if (kPreK) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) kop[c][db] = kt_operand(sm.k[buf], c, db);
+    }
     uint32_t w[16];
     if (DROP) {
 #pragma unroll
@@ -656,18 +674,12 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
       }
 
     // ---- dQ^T += K^T dS^T; K^T operand through LDS transpose reads
-    const bf16* kb_ = sm.k[buf];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bf16x8 dsop = __builtin_bit_cast(bf16x8, make_uint4(dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]));
-      const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kKS + ktr;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const s16x4 lo = lds_read_tr16(&kb_[r0 + 32 * db]);
-        const s16x4 hi = lds_read_tr16(&kb_[r0 + 8 * kKS + 32 * db]);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        qacc[db] = mfma32(a, dsop, qacc[db]);
-      }
+      for (int db = 0; db < kDB; ++db)
+        qacc[db] = mfma32(kPreK ? kop[c][db] : kt_operand(sm.k[buf], c, db), dsop, qacc[db]);
     }
   };
 

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   constexpr int kDC = D / 16;        // 16-wide d chunks (QK^T k-steps)
   constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int kLoads = D / 32;     // 16-byte global loads per thread per tile (each of K, V)
+  constexpr bool kPreV = D >= 128;   // V^T operands read one phase early (registers allow it)
   __shared__ FwdSmem<D> sm;
 
   const int nqt = (p.s + kBM - 1) / kBM;
@@ -224,6 +225,14 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   const int krow = col * kKS + 8 * half;   // K tile rows are in slot order
   const int grp = lane >> 4, lg = lane & 15;
   const int vrow = (16 * (grp >> 1) + (lg >> 2)) * kVS + 16 * (grp & 1) + 4 * (lg & 3);
+  // V^T A operand of PV step c (keys 32(c/2) + 8(c%2) ..), d block db, from a
+  // row-major V tile through two transposing reads
+  auto v_operand = [&](const bf16* vb, int c, int db) -> bf16x8 {
+    const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kVS + vrow;
+    const s16x4 lo = lds_read_tr16(&vb[r0 + 32 * db]);
+    const s16x4 hi = lds_read_tr16(&vb[r0 + 4 * kVS + 32 * db]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   // S^T = K Q^T (raw scores) of the tile in K buffer `buf`, two 32-key blocks
   auto qk = [&](int buf, f32x16 (&s)[2]) {
@@ -306,6 +315,15 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     // ---- next tile's scores on the matrix cores
     f32x16 snext[2];
     if (NEXT) qk((kt + 1) & 1, snext);
+    // with one wave per SIMD nothing else hides the LDS latency of the V^T
+    // operands, so they are read here, behind the exp work of this phase
+    bf16x8 vop[kPreV ? 4 : 1][kPreV ? kDB : 1];
+    if (kPreV) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) vop[c][db] = v_operand(sm.v[kt & 1], c, db);
+    }
 
     // ---- p = exp2(s * c - m), row sum of the undropped values, dropout
     // (1/(1-p) is applied in the epilogue), P^T as bf16 B operands
@@ -336,18 +354,11 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
     // ---- O^T += V^T P^T; V^T operand via LDS transpose reads:
     // lane group G = lane/16 covers d = 32db + 16*(G%2) + (0..15) and the keys
     // 32*kb + 16*(G/2) + 8*c' + (0..7) of step c = 2*kb + c'.
-    const bf16* vb = sm.v[kt & 1];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kVS + vrow;
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const s16x4 lo = lds_read_tr16(&vb[r0 + 32 * db]);
-        const s16x4 hi = lds_read_tr16(&vb[r0 + 4 * kVS + 32 * db]);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma32(a, pop[c], oacc[db]);
-      }
-    }
+      for (int db = 0; db < kDB; ++db)
+        oacc[db] = mfma32(kPreV ? vop[c][db] : v_operand(sm.v[kt & 1], c, db), pop[c], oacc[db]);
     if (NEXT) {
       if (DROP) draws(kt + 1, wcur);
       scur[0] = snext[0];
