@@ -24,6 +24,7 @@ consistent; the pages print only the totals.
 from __future__ import annotations
 
 from dataclasses import dataclass
+from fractions import Fraction
 
 REPLICATED_PER_SBH = 10        # LN inputs (4) + post-attn/MLP dropout masks (2) + QKV/fc1 inputs (4)
 SPLIT_PER_SBH = 24             # the rest of the 34
@@ -105,3 +106,59 @@ def kept_bytes_this_library(s, b, hq, d_head, dtype_bytes=2, norm="layernorm"):
     lse = 4 * b * hq * s
     stats = (8 if norm == "layernorm" else 4) * s * b
     return qkvo + lse + stats
+
+
+# ---- recompute policy: a per-layer choice of none / selective / full ----------
+# The plate's last paragraphs: frameworks expose a dial between selective and
+# full recomputation, full recomputation being for when memory binds.  The
+# plan below is the plain definition of that dial: of all assignments of the
+# three policies to the layers, the one with the least extra compute whose
+# stored bytes fit the budget (ties: fewer stored bytes, then fewer fully
+# recomputed layers).  Exact rational arithmetic, brute force over counts.
+
+POLICIES = ("none", "selective", "full")
+
+
+def layer_bytes_exact(s, b, h, a, t, sequence_parallel, policy) -> Fraction:
+    """Bytes one layer stores on one of t tensor-parallel ranks.
+
+    none / selective follow bytes_tp / bytes_tp_sp above; full keeps the layer
+    input, 2sbh, whole under tensor parallelism alone and its s/t slice with
+    sequence parallelism (reading: the input sits in the sequence-parallel
+    region)."""
+    sbh = Fraction(s * b * h)
+    if policy == "full":
+        return 2 * sbh / t if sequence_parallel else 2 * sbh
+    attn = Fraction(ATTN_SCORE_PER_AS2B * a * s * s * b) if policy == "none" else Fraction(0)
+    if sequence_parallel:
+        return (34 * sbh + attn) / t
+    return REPLICATED_PER_SBH * sbh + (SPLIT_PER_SBH * sbh + attn) / t
+
+
+def extra_compute_exact(s, h, layers, n_params, causal, n_selective, n_full) -> Fraction:
+    """Extra FLOPs over the training FLOPs when n_selective layers re-do their
+    attention-score FLOPs (A = 4sh per token, 2sh causal) and n_full layers
+    re-do their whole forward pass (2N/L + A: 6N -> 8N per token when all do).
+    Base: 6N + 3LA (the base of selective_recompute_extra above)."""
+    A = Fraction((2 if causal else 4) * s * h)
+    per_full = Fraction(2 * n_params, layers) + A
+    return (n_selective * A + n_full * per_full) / (6 * n_params + 3 * layers * A)
+
+
+def plan_recompute(budget, *, s, b, h, a, layers, n_params=0, t=1, sequence_parallel=False,
+                   causal=True):
+    """Returns (n_none, n_selective, n_full, bytes, extra) or None if nothing fits."""
+    budget = Fraction(budget)
+    mem = {p: layer_bytes_exact(s, b, h, a, t, sequence_parallel, p) for p in POLICIES}
+    best = None
+    for n_full in range(layers + 1):
+        for n_sel in range(layers - n_full + 1):
+            n_none = layers - n_full - n_sel
+            m = n_none * mem["none"] + n_sel * mem["selective"] + n_full * mem["full"]
+            if m > budget:
+                continue
+            x = extra_compute_exact(s, h, layers, n_params, causal, n_sel, n_full)
+            key = (x, m, n_full)
+            if best is None or key < best[0]:
+                best = (key, (n_none, n_sel, n_full, m, x))
+    return None if best is None else best[1]

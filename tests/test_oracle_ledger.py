@@ -1,6 +1,7 @@
 """Pins for the activation-memory ledger: the pages' printed example and formulas."""
 import json
 import os
+from fractions import Fraction
 
 import pytest
 
@@ -90,3 +91,79 @@ def test_this_library_keeps_no_s2_term():
     a = lg.kept_bytes_this_library(s=2048, b=1, hq=12, d_head=128)
     b = lg.kept_bytes_this_library(s=4096, b=1, hq=12, d_head=128)
     assert b == pytest.approx(2 * a)          # linear in s
+
+
+# ---- the recompute-policy planner (a dial between none / selective / full)
+
+
+def _llama(golden):
+    d, L = _dims(golden)
+    return dict(s=d.s, b=d.b, h=d.h, a=d.a, layers=L, n_params=70 * 10**9, causal=True)
+
+
+def test_planner_reproduces_the_printed_strategies(golden):
+    """The plate's three strategies are the plans at budgets equal to the bytes it
+    prints for them (within its rounding): 1.9 TB keeps everything, 182.5 GB is
+    selective for 2.4% more compute, 10.7 GB is full for 33% more."""
+    kw, pr, tol = _llama(golden), golden["printed"], golden["printed_precision"]
+    L = kw["layers"]
+    n, s_, f, m, x = lg.plan_recompute(pr["none_bytes"] + tol["none_bytes"], **kw)
+    assert (n, s_, f) == (L, 0, 0) and x == 0
+    n, s_, f, m, x = lg.plan_recompute(pr["selective_bytes"] + tol["selective_bytes"], **kw)
+    assert (n, s_, f) == (0, L, 0)
+    assert round(100 * float(x), 1) == pr["selective_extra_compute_pct"]
+    n, s_, f, m, x = lg.plan_recompute(pr["full_bytes"] + tol["full_bytes"], **kw)
+    assert (n, s_, f) == (0, 0, L)
+    assert abs(100 * float(x) - pr["full_extra_compute_pct"]) <= 0.5
+    assert lg.plan_recompute(0.99 * (pr["full_bytes"] - tol["full_bytes"]), **kw) is None
+
+
+def test_exact_layer_bytes_agree_with_the_pinned_formulas():
+    for s, b, h, a in ((2048, 4, 6144, 64), (8192, 1, 8192, 64), (2048, 1, 20480, 128)):
+        d = lg.LayerDims(s=s, b=b, h=h, a=a)
+        for t in (1, 2, 8):
+            for sel, pol in ((False, "none"), (True, "selective")):
+                assert float(lg.layer_bytes_exact(s, b, h, a, t, False, pol)) == pytest.approx(lg.bytes_tp(d, t, sel), rel=1e-14)
+                assert float(lg.layer_bytes_exact(s, b, h, a, t, True, pol)) == pytest.approx(lg.bytes_tp_sp(d, t, sel), rel=1e-14)
+        assert float(lg.layer_bytes_exact(s, b, h, a, 1, False, "full")) == lg.bytes_full(d)
+        assert float(lg.layer_bytes_exact(s, b, h, a, 1, False, "none")) == pytest.approx(lg.bytes_none(d), rel=1e-14)
+
+
+def test_extra_compute_end_points():
+    # all layers full: a second forward pass, 6N -> 8N, exactly a third more
+    for causal in (True, False):
+        assert lg.extra_compute_exact(4096, 5120, 40, 13 * 10**9, causal, 0, 40) == Fraction(1, 3)
+    # all layers selective: the score FLOPs re-done, the reading pinned above
+    d = lg.LayerDims(s=8192, b=1, h=8192, a=64)
+    x = lg.extra_compute_exact(d.s, d.h, 80, 70 * 10**9, True, 80, 0)
+    assert float(x) == pytest.approx(lg.selective_recompute_extra(70e9, d, 80, causal=True), rel=1e-12)
+
+
+def test_single_layer_takes_the_first_policy_that_fits():
+    kw = dict(s=1024, b=2, h=1024, a=16, layers=1, n_params=10**8)
+    mem = {p: lg.layer_bytes_exact(1024, 2, 1024, 16, 1, False, p) for p in lg.POLICIES}
+    for budget, want in ((mem["none"], (1, 0, 0)), (mem["none"] - 1, (0, 1, 0)), (mem["selective"], (0, 1, 0)),
+                         (mem["selective"] - 1, (0, 0, 1)), (mem["full"], (0, 0, 1))):
+        assert lg.plan_recompute(budget, **kw)[:3] == want
+    assert lg.plan_recompute(mem["full"] - 1, **kw) is None
+
+
+def test_plans_fit_are_monotone_and_locally_optimal():
+    kw = dict(s=2048, b=1, h=4096, a=32, layers=12, n_params=2 * 10**9, t=2, sequence_parallel=True)
+    mem = {p: lg.layer_bytes_exact(2048, 1, 4096, 32, 2, True, p) for p in lg.POLICIES}
+    lo, hi = 12 * mem["full"], 12 * mem["none"]
+    prev = None
+    for k in range(41):
+        budget = lo + (hi - lo) * Fraction(k, 40)
+        n, s_, f, m, x = lg.plan_recompute(budget, **kw)
+        assert n + s_ + f == 12 and m <= budget
+        assert m == n * mem["none"] + s_ * mem["selective"] + f * mem["full"]
+        # one layer moved to a cheaper policy no longer fits
+        if f:
+            assert m - mem["full"] + mem["selective"] > budget or lg.extra_compute_exact(
+                2048, 4096, 12, 2 * 10**9, True, s_ + 1, f - 1) >= x
+        if s_:
+            assert m - mem["selective"] + mem["none"] > budget
+        if prev is not None:
+            assert x <= prev
+        prev = x
