@@ -224,6 +224,64 @@ int srat_trace_enable(int on);
 typedef struct { char name[48]; int64_t launches; double total_ms; } srat_trace_entry;
 int srat_trace_read(srat_trace_entry* out, int cap, int reset);
 
+/*
+ * Recompute policy: the activation-memory ledger of a transformer layer and a
+ * planner that picks, layer by layer, what to keep and what to recompute.
+ * Host-only (no HIP call, no device pointer).
+ *
+ * Stored activation bytes of one layer, 2-byte activations ("Recomputing
+ * Activations" plate, "What you will learn": 34d + 5HT bytes per token per
+ * layer with nothing recomputed, 34d with the attention scores recomputed,
+ * 2d with only each layer's input kept):
+ *   SRAT_RECOMPUTE_NONE       sbh(34 + 5as/h)
+ *   SRAT_RECOMPUTE_SELECTIVE  34sbh        (the attention core is recomputed,
+ *                                           what srat_attn_core_bwd does)
+ *   SRAT_RECOMPUTE_FULL       2sbh         (the layer input only)
+ * On one of t tensor-parallel ranks the layer norms and the dropouts after
+ * attention and the MLP (10sbh) stay whole and the rest divides by t; with
+ * sequence parallelism everything divides by t (LIT-736 record, Key
+ * takeaways bullets 1-2).  Reading: a fully recomputed layer keeps its input
+ * whole under tensor parallelism alone and its s/t slice with sequence
+ * parallelism (the input sits in the sequence-parallel region).
+ *
+ * Extra compute, per token over the layers described: selective re-does the
+ * attention-score FLOPs of the forward pass, A = 4sh per layer (2sh causal);
+ * full re-does the whole forward pass of the layer, 2N/L + A (training goes
+ * from about 6N to 8N FLOPs per token, the plate's second paragraph).  The
+ * base is the training FLOPs 6N + 3LA (forward plus backward of the weights
+ * and of the attention scores).  All of it divides by t, so the fractions do
+ * not depend on t.
+ */
+enum srat_recompute_policy { SRAT_RECOMPUTE_NONE = 0, SRAT_RECOMPUTE_SELECTIVE = 1, SRAT_RECOMPUTE_FULL = 2 };
+
+typedef struct {
+  int64_t s, b, h, a;          /* sequence length, micro-batch, hidden size, attention heads (all > 0) */
+  int64_t layers;              /* layers held on this device (> 0) */
+  int64_t n_params;            /* parameters N of those layers (>= 0; 0 counts attention FLOPs only) */
+  int64_t t;                   /* tensor-parallel size (>= 1) */
+  int32_t sequence_parallel;   /* 0/1 */
+  int32_t causal;              /* 0/1: causal attention computes half the scores */
+} srat_layer_desc;
+
+typedef struct {
+  int64_t layers_none, layers_selective, layers_full;   /* sum = desc->layers */
+  double activation_bytes;     /* stored on this device, all layers */
+  double extra_compute;        /* extra FLOPs / base training FLOPs */
+} srat_recompute_plan;
+
+/* Bytes one layer stores on this device under `policy`, and the extra-compute
+ * fraction that policy costs when every layer uses it.  Either output may be
+ * NULL. */
+int srat_activation_bytes(const srat_layer_desc* desc, int policy, double* bytes_per_layer,
+                          double* extra_compute);
+
+/* The assignment of policies to layers with the least extra compute whose
+ * stored bytes fit `budget_bytes` (ties: fewer stored bytes, then fewer fully
+ * recomputed layers); layers differ only in count.  Exact integer arithmetic.
+ * SRAT_ERR_UNSUPPORTED (plan zeroed) when even full recomputation of every
+ * layer does not fit. */
+int srat_plan_recompute(const srat_layer_desc* desc, double budget_bytes, srat_recompute_plan* plan);
+
 /* Thread-local text of the last error of this thread ("" if none). */
 const char* srat_last_error(void);
 int srat_version(void);

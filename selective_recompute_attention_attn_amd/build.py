@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsrat.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["abi.cpp", "sp_norm.hip", "attn_f32.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["abi.cpp", "recompute.cpp", "sp_norm.hip", "attn_f32.hip", "attn_fwd.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -208,6 +208,11 @@ int attn_fwd_impl(const srat_attn_desc* desc, const void* q, const void* k, cons
 }  // namespace
 
 namespace srat {
+int activation_bytes(const srat_layer_desc* d, int policy, double* bytes, double* extra, std::string* err);
+int plan_recompute(const srat_layer_desc* d, double budget, srat_recompute_plan* plan, std::string* err);
+}  // namespace srat
+
+namespace srat {
 
 TraceScope::TraceScope(const char* name, hipStream_t st) : name_(name), st_(st) {
   ev_[0] = ev_[1] = nullptr;
@@ -425,6 +430,22 @@ int srat_trace_read(srat_trace_entry* out, int cap, int reset) {
   }
   if (reset) t.acc.clear();
   return n;
+}
+
+// ---- recompute policy (host only)
+int srat_activation_bytes(const srat_layer_desc* desc, int policy, double* bytes_per_layer,
+                          double* extra_compute) {
+  std::string err;
+  const int rc = srat::activation_bytes(desc, policy, bytes_per_layer, extra_compute, &err);
+  if (rc != SRAT_OK) return fail(rc, "%s", err.c_str());
+  return SRAT_OK;
+}
+
+int srat_plan_recompute(const srat_layer_desc* desc, double budget_bytes, srat_recompute_plan* plan) {
+  std::string err;
+  const int rc = srat::plan_recompute(desc, budget_bytes, plan, &err);
+  if (rc != SRAT_OK) return fail(rc, "%s", err.c_str());
+  return SRAT_OK;
 }
 
 }  // extern "C"

@@ -23,7 +23,9 @@ SRAT_LAYERNORM, SRAT_RMSNORM = 1, 2
 ERRORS = {-1: "SRAT_ERR_INVALID", -2: "SRAT_ERR_UNSUPPORTED", -3: "SRAT_ERR_WORKSPACE", -4: "SRAT_ERR_HIP"}
 EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_fwd_workspace", "srat_attn_core_fwd_ws", "srat_attn_core_bwd", "srat_attn_core_bwd_workspace", "srat_sp_norm_fwd",
            "srat_sp_norm_bwd", "srat_sp_norm_bwd_workspace", "srat_dropout_mask_dump", "srat_trace_enable",
-           "srat_trace_read", "srat_last_error", "srat_version")
+           "srat_trace_read", "srat_last_error", "srat_version", "srat_activation_bytes",
+           "srat_plan_recompute")
+RECOMPUTE_POLICIES = {"none": 0, "selective": 1, "full": 2}
 
 
 class AttnDesc(ctypes.Structure):
@@ -41,6 +43,18 @@ class NormDesc(ctypes.Structure):
                 ("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("h", ctypes.c_int64),
                 ("seq_offset", ctypes.c_int64), ("eps", ctypes.c_float), ("p_drop", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("site", ctypes.c_int32)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_int64), ("b", ctypes.c_int64), ("h", ctypes.c_int64), ("a", ctypes.c_int64),
+                ("layers", ctypes.c_int64), ("n_params", ctypes.c_int64), ("t", ctypes.c_int64),
+                ("sequence_parallel", ctypes.c_int32), ("causal", ctypes.c_int32)]
+
+
+class RecomputePlan(ctypes.Structure):
+    _fields_ = [("layers_none", ctypes.c_int64), ("layers_selective", ctypes.c_int64),
+                ("layers_full", ctypes.c_int64), ("activation_bytes", ctypes.c_double),
+                ("extra_compute", ctypes.c_double)]
 
 
 class TraceEntry(ctypes.Structure):
@@ -74,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.srat_dropout_mask_dump.argtypes = [ctypes.c_int, vp, vp, vp]
         L.srat_trace_enable.argtypes = [ctypes.c_int]
         L.srat_trace_read.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int, ctypes.c_int]
+        dp = ctypes.POINTER(ctypes.c_double)
+        L.srat_activation_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int, dp, dp]
+        L.srat_plan_recompute.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double, ctypes.POINTER(RecomputePlan)]
         L.srat_last_error.restype = ctypes.c_char_p
         for f in EXPORTS:
             if f != "srat_last_error":
@@ -372,3 +389,30 @@ def trace_read(reset: bool = True):
     if n < 0:
         _check(n, "srat_trace_read")
     return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, cap))}
+
+
+# ---- recompute policy (host only: no device, no stream)
+def layer_desc(*, s: int, b: int, h: int, a: int, layers: int, n_params: int = 0, t: int = 1,
+               sequence_parallel: bool = False, causal: bool = True) -> LayerDesc:
+    return LayerDesc(s, b, h, a, layers, int(n_params), t, int(bool(sequence_parallel)), int(bool(causal)))
+
+
+def activation_bytes(policy: str, **dims) -> Tuple[float, float]:
+    """(bytes one layer stores on this device, extra-compute fraction) when every
+    layer uses `policy` ("none", "selective" or "full")."""
+    d = layer_desc(**dims)
+    nb, ex = ctypes.c_double(), ctypes.c_double()
+    _check(lib().srat_activation_bytes(ctypes.byref(d), RECOMPUTE_POLICIES[policy], ctypes.byref(nb),
+                                       ctypes.byref(ex)), "srat_activation_bytes")
+    return nb.value, ex.value
+
+
+def plan_recompute(budget_bytes: float, **dims) -> dict:
+    """Least-extra-compute assignment of none / selective / full recomputation to
+    the layers whose stored activations fit `budget_bytes` on this device."""
+    d = layer_desc(**dims)
+    plan = RecomputePlan()
+    _check(lib().srat_plan_recompute(ctypes.byref(d), float(budget_bytes), ctypes.byref(plan)),
+           "srat_plan_recompute")
+    return {"none": plan.layers_none, "selective": plan.layers_selective, "full": plan.layers_full,
+            "activation_bytes": plan.activation_bytes, "extra_compute": plan.extra_compute}
