@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
       }
   };
 
-  const uint32_t thr_hi = p.thresh << 16;
+  const uint32_t tm1 = (p.thresh - 1u) * 0x10001u;   // T - 1 in both halves (T >= 1 when DROP)
   const float c2 = p.scale_log2;
 
   // one tile: MASK = causal / tail masking needed, NEXT = tile kt+1 exists
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
         uint32_t pk = pack_bf16x2(e0, e1);
         if (DROP) {   // zero the dropped halves of the packed pair
           const uint32_t w = wcur[8 * kb + (r >> 1)];
-          pk = and_or(pk, (w & 0xFFFFu) >= p.thresh ? 0xFFFFu : 0u, w >= thr_hi ? 0xFFFF0000u : 0u);
+          pk = drop_pair(pk, w, tm1);
         }
         pw[8 * kb + (r >> 1)] = pk;
       }

@@ -64,6 +64,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, b, c, 0xE0);
 }
+// Dropout of a packed bf16 pair by a packed pair of 16-bit draws w: each half
+// of `pair` is kept iff its draw is >= T, given tm1 = (T-1) in both halves
+// (T >= 1, wave-uniform).  Three packed 16-bit ops: the saturating difference
+// draw - (T-1) is 0 exactly for the dropped halves, its minimum with 1 is the
+// keep bit, and the 16-bit product of a half's bits with that bit keeps or
+// clears it.  Written as instructions because the compiler turns the same
+// expression in C into per-half compares and selects (five ops).  ALU only.
+__device__ __forceinline__ uint32_t drop_pair(uint32_t pair, uint32_t w, uint32_t tm1) {
+  uint32_t d, k, r;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(w), "s"(tm1));
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(k) : "v"(d), "s"(0x00010001u));
+  asm("v_pk_mul_lo_u16 %0, %1, %2" : "=v"(r) : "v"(pair), "v"(k));
+  return r;
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
