@@ -8,9 +8,11 @@ already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-value       attention-core fwd+bwd algorithmic TFLOP/s, timed with HIP events
-            (timing-only, no system fence) around the attention calls of each
-            timed step
+ms_per_step wall clock of the K timed steps (synchronised on both sides)
+value       attention-core fwd+bwd algorithmic TFLOP/s over K back-to-back
+            fwd+bwd passes on the rotating buffer sets, timed by one pair of
+            HIP events (timing-only, no system fence) on the launch stream;
+            the norm region's GB/s likewise over K back-to-back passes each
 roofline    the dominant kernel (largest share of the traced time): its
             algorithmic work per launch / its mean launch time, against
             MI355X's published peak.  Launch times come from the library's
@@ -33,7 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attn-core fwd+bwd TFLOP/s & % bf16 MFMA peak; SP LayerNorm GB/s (1 GPU)"
 PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_HBM_GBPS = 8000.0
-N_SETS = 4                      # rotated input/output sets (> 2x the 256 MB last-level cache)
+N_SETS = 8                      # rotated input/output sets: a set's inputs have left the
+                                # 256 MB last-level cache before it is used again
 COPY_CALIBRATION_BYTES = 1 << 29  # 512 MiB read + 512 MiB written per calibration copy
 COPY_CALIBRATION_REPS = 3
 
@@ -241,20 +244,36 @@ def main():
             ops.prepare_sp_norm_fwd(s["resid"], s["y"], s["gamma"], s["beta"], h, u, mu, rs, eps=n.eps, **nkw),
             ops.prepare_sp_norm_bwd(s["du"], s["dres"], h, s["gamma"], mu, rs, *s["nb"], ws_norm, **nkw)))
 
-    def step(i, ev=None):
+    def step(i):
         fwd, bwd, nfwd, nbwd = calls[i % N_SETS]
-        if ev is not None:
-            ev[0].record()
         fwd()
         bwd()
-        if ev is not None:
-            ev[1].record()
         nfwd()
-        if ev is not None:
-            ev[2].record()
         nbwd()
-        if ev is not None:
-            ev[3].record()
+
+    def attn_pass(i):
+        fwd, bwd, _, _ = calls[i % N_SETS]
+        fwd()
+        bwd()
+
+    def norm_fwd_pass(i):
+        calls[i % N_SETS][2]()
+
+    def norm_bwd_pass(i):
+        calls[i % N_SETS][3]()
+
+    def region_ms(fn, k):
+        """Mean time of one of k back-to-back calls of fn, from one event pair
+        on the launch stream: a timing event recorded between kernels leaves
+        the GPU idle for a few microseconds, so none sits inside the region."""
+        ev0, ev1 = TimingEvent(stream), TimingEvent(stream)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(k):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / k
 
     if args.calibrate_copy:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
@@ -267,13 +286,18 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    evs = [[TimingEvent(stream) for _ in range(4)] for _ in range(args.steps)]
+    # the K timed steps (wall clock, synchronised on both sides)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # the attention core and the norm region, each as K back-to-back passes
+    # over the same rotating buffer sets
+    attn_ms = region_ms(attn_pass, args.steps)
+    nf_ms = region_ms(norm_fwd_pass, args.steps)
+    nb_ms = region_ms(norm_bwd_pass, args.steps)
     # per-kernel durations come from a second pass over the same K steps with
     # the library's launch trace on: its two events per launch add a few
     # microseconds between kernels, so they stay out of the timed region above
@@ -287,9 +311,6 @@ def main():
         trace = ops.trace_read(reset=True)
         ops.trace_enable(False)
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    nf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    nb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     flops = attn_flops(a)
     value = flops / (attn_ms * 1e-3) / 1e12
 
