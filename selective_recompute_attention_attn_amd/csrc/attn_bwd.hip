@@ -91,11 +91,13 @@ constexpr int kWaveTile = 32 * kWaveRow;
 //   d <= 64 : two query halves (8 waves, 2 per SIMD), K and V rows in registers;
 //   d == 96 : one query half (4 waves), V rows read from LDS so that a wave
 //             fits 256 registers and two workgroups share a CU;
-//   d >= 128: one query half, one workgroup per CU (accumulators in AGPRs).
+//   d >= 128: one query half, one workgroup per CU (accumulators in AGPRs);
+//   d >= 192: V rows again through LDS, so that K, the dK/dV accumulators and
+//             the tile's values fit the 512 registers of a wave.
 template <int D> struct DkdvCfg {
   static constexpr int kQH = D <= 64 ? 2 : 1;
-  static constexpr bool kVLds = D == 96;
-  static constexpr int kBlocksPerCU = kVLds ? 2 : 1;
+  static constexpr bool kVLds = D == 96 || D >= 192;
+  static constexpr int kBlocksPerCU = D == 96 ? 2 : 1;
 };
 
 template <int D, int QH>
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   // the lane's two Philox calls cover keys kw0 + 16half + 8gh .. +7 of its
   // query: fixed key group, the query varies by tile
   // (hoisted state costs 18 registers: only where the waves have room)
-  constexpr bool kHoist = QH == 1;
+  constexpr bool kHoist = QH == 1 && D < 192;   // (at d >= 192 its registers are worth more)
   PhiloxCol pcol[2];
   if (DROP && kHoist) {
 #pragma unroll
@@ -873,6 +875,7 @@ hipError_t launch_attn_bwd(const AttnParams& p, bool bf16_path, hipStream_t st) 
     case 96: return bwd_launch_d<96>(p, st);
     case 128: return bwd_launch_d<128>(p, st);
     case 160: return bwd_launch_d<160>(p, st);
+    case 192: return bwd_launch_d<192>(p, st);
   }
   return hipErrorInvalidValue;
 }

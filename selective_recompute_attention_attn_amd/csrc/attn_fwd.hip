@@ -516,6 +516,7 @@ hipError_t launch_attn_fwd(const AttnParams& p, bool bf16_path, hipStream_t st) 
     case 96: return fwd_launch_d<96>(p, st);
     case 128: return fwd_launch_d<128>(p, st);
     case 160: return fwd_launch_d<160>(p, st);
+    case 192: return fwd_launch_d<192>(p, st);
   }
   return hipErrorInvalidValue;
 }
