@@ -99,9 +99,8 @@ def cpu_baseline(w, seconds_budget=15.0):
     x = gen.attn_inputs(a)
     kw = dict(causal=a.causal, scale=a.scale, p_drop=a.p_drop, seed=a.seed)
     heads, t_attn = [], 0.0
-    grp = a.hq // a.hkv
     for bb in range(a.b):
-        for hh in range(0, a.hq, grp):
+        for hh in range(a.hq):
             t0 = time.perf_counter()
             o, lse = oat.attn_fwd(x["q"], x["k"], x["v"], heads=[(bb, hh)], **kw)
             oat.attn_bwd(x["q"], x["k"], x["v"], lse, x["do"], heads=[(bb, hh)], **kw)
