@@ -89,7 +89,7 @@ enum srat_norm_kind { SRAT_LAYERNORM = 1, SRAT_RMSNORM = 2 };
 typedef struct {
   int32_t dtype;          /* SRAT_BF16 (MFMA path) or SRAT_F32 (reference-precision path) */
   int32_t causal;         /* 1: key j is visible to query i iff j <= i; 0: all keys visible */
-  int64_t b, s, hq, hkv, d;  /* d in {32, 64, 96, 128, 160}, and 192 for bf16; hq % hkv == 0; s >= 1 */
+  int64_t b, s, hq, hkv, d;  /* d in {32, 64, 96, 128, 160}, and 192, 256 for bf16; hq % hkv == 0; s >= 1 */
   int64_t q_stride[3];    /* (batch, seq, head) strides of Q, dQ */
   int64_t k_stride[3];    /* ... of K, dK */
   int64_t v_stride[3];    /* ... of V, dV */

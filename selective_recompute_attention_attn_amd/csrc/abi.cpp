@@ -70,10 +70,10 @@ int check_attn(const srat_attn_desc* d) {
   if (d->causal != 0 && d->causal != 1) return fail(SRAT_ERR_INVALID, "causal must be 0 or 1");
   if (d->b < 0 || d->s < 0 || d->hq <= 0 || d->hkv <= 0) return fail(SRAT_ERR_INVALID, "negative or zero size");
   if (d->hq % d->hkv) return fail(SRAT_ERR_INVALID, "hq (%lld) not a multiple of hkv (%lld)", (long long)d->hq, (long long)d->hkv);
-  if (d->d != 32 && d->d != 64 && d->d != 96 && d->d != 128 && d->d != 160 && d->d != 192)
-    return fail(SRAT_ERR_UNSUPPORTED, "head dim %lld not in {32,64,96,128,160,192}", (long long)d->d);
-  if (d->d == 192 && d->dtype != SRAT_BF16)
-    return fail(SRAT_ERR_UNSUPPORTED, "head dim 192 is implemented for bf16 only");
+  if (d->d != 32 && d->d != 64 && d->d != 96 && d->d != 128 && d->d != 160 && d->d != 192 && d->d != 256)
+    return fail(SRAT_ERR_UNSUPPORTED, "head dim %lld not in {32,64,96,128,160,192,256}", (long long)d->d);
+  if (d->d > 160 && d->dtype != SRAT_BF16)
+    return fail(SRAT_ERR_UNSUPPORTED, "head dims above 160 are implemented for bf16 only");
   if (d->s > (1 << 30) || d->b > (1 << 20) || d->hq > (1 << 16))
     return fail(SRAT_ERR_UNSUPPORTED, "size beyond the 32-bit counter ranges");
   if (d->head_offset < 0 || d->head_offset + d->hq > ((int64_t)1 << 31))

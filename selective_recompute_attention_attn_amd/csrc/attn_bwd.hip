@@ -92,12 +92,17 @@ constexpr int kWaveTile = 32 * kWaveRow;
 //   d == 96 : one query half (4 waves), V rows read from LDS so that a wave
 //             fits 256 registers and two workgroups share a CU;
 //   d >= 128: one query half, one workgroup per CU (accumulators in AGPRs);
-//   d >= 192: V rows again through LDS, so that K, the dK/dV accumulators and
-//             the tile's values fit the 512 registers of a wave.
+//   d == 192: V rows again through LDS, so that K, the dK/dV accumulators and
+//             the tile's values fit the 512 registers of a wave;
+//   d == 256: two workgroups per key block, each accumulating and storing
+//             half of dK's and dV's columns (both recompute S and dP over
+//             the whole head dim): the accumulators of all 256 columns alone
+//             would take half of a wave's registers.
 template <int D> struct DkdvCfg {
   static constexpr int kQH = D <= 64 ? 2 : 1;
-  static constexpr bool kVLds = D == 96 || D >= 192;
+  static constexpr bool kVLds = D == 96 || D == 192;
   static constexpr int kBlocksPerCU = D == 96 ? 2 : 1;
+  static constexpr int kDParts = D >= 256 ? 2 : 1;
 };
 
 template <int D, int QH>
@@ -137,6 +142,8 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   constexpr int kThreads = 256 * QH;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
+  constexpr int kDParts = DkdvCfg<D>::kDParts;
+  constexpr int kDBA = kDB / kDParts;   // 32-column blocks of dK / dV this workgroup accumulates
   constexpr int kTileChunks = kRows * D / 8;
   constexpr int kTileLoads = (kTileChunks + kThreads - 1) / kThreads;
   __shared__ SM sm;
@@ -148,7 +155,10 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   // descending, so the workgroups that share a CU (block i and i + grid/2)
   // together carry the same number of query tiles.
   const int nkb = (p.s + kBNk - 1) / kBNk;
-  const int rank = (int)(blockIdx.x / nbh);
+  const int dpart = (int)(blockIdx.x % kDParts);        // which columns of dK / dV
+  const int wg = (int)(blockIdx.x / kDParts);
+  const int d0 = dpart * kDBA;                           // first 32-column block of them
+  const int rank = wg / nbh;
   const int hkb = (nkb + 1) / 2;
   // Split grids (p.split_kb > 0, causal only): the split_kb blocks with the
   // most queries (the lowest keys) run as two workgroups each (part 0: the
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     const bool mirror = CAUSAL && DkdvCfg<D>::kBlocksPerCU == 2 && rank >= hkb;
     kblk = mirror ? nkb - 1 - (rank - hkb) : rank;
   }
-  const int bh = blockIdx.x % nbh;
+  const int bh = wg % nbh;
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -214,9 +224,9 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     }
   }
   const int v_row = (32 * kg + col) * SM::kVS + 8 * half;   // this lane's V row in LDS
-  f32x16 dv_acc[kDB], dk_acc[kDB];
+  f32x16 dv_acc[kDBA], dk_acc[kDBA];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
+  for (int db = 0; db < kDBA; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
 
   const int nqt_all = (sl + kRows - 1) / kRows;
   const int qt_first = CAUSAL ? k0 / kRows : 0;
@@ -365,9 +375,9 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
       const bf16x8 apm = tr_pair(&pmt[16 * st * kWaveRow + tr_w], kWaveRow);
       const bf16x8 ads = tr_pair(&dst[16 * st * kWaveRow + tr_w], kWaveRow);
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        dv_acc[db] = mfma32(apm, tr_pair(&ob_[16 * st * kS + tr_s + 32 * db], kS), dv_acc[db]);
-        dk_acc[db] = mfma32(ads, tr_pair(&qb_[16 * st * kS + tr_s + 32 * db], kS), dk_acc[db]);
+      for (int db = 0; db < kDBA; ++db) {
+        dv_acc[db] = mfma32(apm, tr_pair(&ob_[16 * st * kS + tr_s + 32 * (d0 + db)], kS), dv_acc[db]);
+        dk_acc[db] = mfma32(ads, tr_pair(&qb_[16 * st * kS + tr_s + 32 * (d0 + db)], kS), dk_acc[db]);
       }
     }
   };
@@ -405,14 +415,14 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
       __syncthreads();
       if (qh == 1) {
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
+        for (int db = 0; db < kDBA; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sm.comb[kg][(db * 16 + r) * 64 + lane] = which ? dk_acc[db][r] : dv_acc[db][r];
       }
       __syncthreads();
       if (qh == 0) {
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
+        for (int db = 0; db < kDBA; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float x = sm.comb[kg][(db * 16 + r) * 64 + lane];
@@ -424,16 +434,16 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
     if (qh == 1) return;
   }
 
-  // store: lane holds d = 32db + col, keys kw0 + 8*(r/4) + 4*half + r%4
+  // store: lane holds d = 32(d0 + db) + col, keys kw0 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) {
+  for (int db = 0; db < kDBA; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (key >= p.s) continue;
       const float dvv = dv_acc[db][r] * p.inv_keep;
       const float dkv = dk_acc[db][r] * p.scale;
-      const int dcol = 32 * db + col;
+      const int dcol = 32 * (d0 + db) + col;
       if (PART || part >= 0) {   // slot 1 holds the second parts of split blocks
         const int64_t o = ((int64_t)max(part, 0) * p.b * p.s * p.hq + ((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
         p.dv_acc[o] = dvv;
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kLoads = D / 32;
-  constexpr bool kPreK = DqOcc<D>::kWavesPerEU == 1;   // K^T operands read one phase early
+  constexpr bool kPreK = DqOcc<D>::kWavesPerEU == 1 && D <= 192;   // K^T operands read one phase early
   __shared__ DqSmem<D> sm;
 
   const int nqt = (p.s + kQM - 1) / kQM;
@@ -815,7 +825,7 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   {
     TraceScope ts("attn_bwd_dkdv", st);
     const unsigned nkb = (unsigned)((p.s + kBNk - 1) / kBNk);
-    const dim3 grid((nkb + p.split_kb) * nbh);
+    const dim3 grid((nkb + p.split_kb) * nbh * DkdvCfg<D>::kDParts);
     const int threads = 256 * DkdvCfg<D>::kQH;
     if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, threads, 0, st>>>(p);
     else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, threads, 0, st>>>(p);
@@ -876,6 +886,7 @@ hipError_t launch_attn_bwd(const AttnParams& p, bool bf16_path, hipStream_t st) 
     case 128: return bwd_launch_d<128>(p, st);
     case 160: return bwd_launch_d<160>(p, st);
     case 192: return bwd_launch_d<192>(p, st);
+    case 256: return bwd_launch_d<256>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   constexpr int kDC = D / 16;        // 16-wide d chunks (QK^T k-steps)
   constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int kLoads = D / 32;     // 16-byte global loads per thread per tile (each of K, V)
-  constexpr bool kPreV = D >= 128;   // V^T operands read one phase early (registers allow it)
+  constexpr bool kPreV = D >= 128 && D <= 192;   // V^T operands read one phase early (registers allow it)
   __shared__ FwdSmem<D> sm;
 
   const int nqt = (p.s + kBM - 1) / kBM;
@@ -517,6 +517,7 @@ hipError_t launch_attn_fwd(const AttnParams& p, bool bf16_path, hipStream_t st) 
     case 128: return fwd_launch_d<128>(p, st);
     case 160: return fwd_launch_d<160>(p, st);
     case 192: return fwd_launch_d<192>(p, st);
+    case 256: return fwd_launch_d<256>(p, st);
   }
   return hipErrorInvalidValue;
 }

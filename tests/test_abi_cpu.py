@@ -56,7 +56,7 @@ def _err(L, rc):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=48), -2), (dict(d=256), -2), (dict(d=192, dtype=ops.SRAT_F32), -2), (dict(p_drop=1.0), -1), (dict(p_drop=-0.1), -1),
+    (dict(d=48), -2), (dict(d=320), -2), (dict(d=192, dtype=ops.SRAT_F32), -2), (dict(d=256, dtype=ops.SRAT_F32), -2), (dict(p_drop=1.0), -1), (dict(p_drop=-0.1), -1),
     (dict(hq=4, hkv=3), -1), (dict(dtype=7), -1), (dict(causal=2), -1), (dict(s=-1), -1),
     (dict(q_stride=(256 * 4 * 64, 4 * 64, 60)), -1), (dict(k_stride=(0, 3, 64)), -1),
     (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1), (dict(scale=0.0), -1),

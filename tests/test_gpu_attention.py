@@ -69,6 +69,8 @@ SMALL = [
     (2, 128, 8, 1, 128, True, 0.0),
     (1, 333, 2, 2, 192, True, 0.1),
     (2, 200, 4, 2, 192, False, 0.0),
+    (1, 300, 2, 2, 256, True, 0.1),
+    (2, 130, 4, 2, 256, False, 0.0),
 ]
 
 
@@ -290,6 +292,7 @@ PADDED = [
     (2, 257, 3, 3, 96, False, 0.2, [256, 33]),
     (2, 384, 2, 1, 160, True, 0.0, [383, 64]),
     (2, 300, 2, 2, 192, True, 0.1, [300, 111]),
+    (2, 260, 2, 1, 256, True, 0.1, [260, 99]),
     (4, 2048, 8, 8, 96, True, 0.1, [2048, 1500, 700, 31]),
 ]
 
