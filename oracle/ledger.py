@@ -109,12 +109,13 @@ def kept_bytes_this_library(s, b, hq, d_head, dtype_bytes=2, norm="layernorm"):
 
 
 # ---- recompute policy: a per-layer choice of none / selective / full ----------
-# The plate's last paragraphs: frameworks expose a dial between selective and
-# full recomputation, full recomputation being for when memory binds.  The
-# plan below is the plain definition of that dial: of all assignments of the
-# three policies to the layers, the one with the least extra compute whose
-# stored bytes fit the budget (ties: fewer stored bytes, then fewer fully
-# recomputed layers).  Exact rational arithmetic, brute force over counts.
+# The plate's closing paragraphs: in practice the choice between selective
+# and full recomputation is left to the user, full recomputation being for
+# when memory binds.  The plan below is the plain definition of that choice
+# made per layer: of all assignments of the three policies to the layers, the
+# one with the least extra compute whose stored bytes fit the budget (ties:
+# fewer stored bytes, then fewer fully recomputed layers).  Exact rational
+# arithmetic, brute force over counts.
 
 POLICIES = ("none", "selective", "full")
 

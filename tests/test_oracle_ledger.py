@@ -93,7 +93,7 @@ def test_this_library_keeps_no_s2_term():
     assert b == pytest.approx(2 * a)          # linear in s
 
 
-# ---- the recompute-policy planner (a dial between none / selective / full)
+# ---- the recompute-policy planner (a per-layer choice of none / selective / full)
 
 
 def _llama(golden):
