@@ -1,6 +1,5 @@
 """The layer around the attention core (layer.py) on the GPU against the
 oracle's float64 layer, and full recomputation against selective."""
-import math
 
 import numpy as np
 import pytest
