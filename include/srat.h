@@ -279,7 +279,7 @@ int srat_activation_bytes(const srat_layer_desc* desc, int policy, double* bytes
  * stored bytes fit `budget_bytes` (ties: fewer stored bytes, then fewer fully
  * recomputed layers); layers differ only in count.  Exact integer arithmetic.
  * SRAT_ERR_UNSUPPORTED (plan zeroed) when even full recomputation of every
- * layer does not fit. */
+ * layer does not fit; SRAT_ERR_INVALID for a negative or NaN budget. */
 int srat_plan_recompute(const srat_layer_desc* desc, double budget_bytes, srat_recompute_plan* plan);
 
 /* Thread-local text of the last error of this thread ("" if none). */

@@ -101,7 +101,7 @@ int plan_recompute(const srat_layer_desc* d, double budget, srat_recompute_plan*
   if (!plan) { *err = "plan is NULL"; return SRAT_ERR_INVALID; }
   *plan = srat_recompute_plan{0, 0, 0, 0.0, 0.0};
   if (!check(d, err)) return SRAT_ERR_INVALID;
-  if (std::isnan(budget)) { *err = "budget is NaN"; return SRAT_ERR_INVALID; }
+  if (std::isnan(budget) || budget < 0) { *err = "budget must be a number >= 0"; return SRAT_ERR_INVALID; }
   const Ledger g = ledger(d);
   const i128 L = g.layers;
   const i128 mn = g.mem_t[SRAT_RECOMPUTE_NONE], ms = g.mem_t[SRAT_RECOMPUTE_SELECTIVE],
@@ -109,7 +109,6 @@ int plan_recompute(const srat_layer_desc* d, double budget, srat_recompute_plan*
   // stored bytes * t must not exceed budget * t; the largest possible need is
   // below 2^120, so larger budgets are "everything fits"
   const long double bt = std::floor((long double)budget * (long double)g.t);
-  if (bt < 0) { *err = "budget is negative"; return SRAT_ERR_UNSUPPORTED; }
   const i128 cap = bt >= 1e36L ? ((i128)1 << 120) : (i128)bt;
 
   // For a fixed number nf of fully recomputed layers, the cheapest fit

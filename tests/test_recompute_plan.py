@@ -90,3 +90,9 @@ def test_unknown_policy_and_null_pointers(L):
     assert L.srat_activation_bytes(None, 0, None, None) == -1
     assert L.srat_activation_bytes(ctypes.byref(d), 0, None, None) == 0
     assert L.srat_plan_recompute(ctypes.byref(d), 1e9, None) == -1
+
+
+@pytest.mark.parametrize("budget", [-1.0, float("nan")])
+def test_negative_or_nan_budget_is_invalid(budget):
+    with pytest.raises(ops.SratError, match="INVALID"):
+        ops.plan_recompute(budget, s=128, b=1, h=64, a=2, layers=2)
