@@ -261,7 +261,9 @@ typedef struct {
   int64_t t;                   /* tensor-parallel size (>= 1) */
   int32_t sequence_parallel;   /* 0/1 */
   int32_t causal;              /* 0/1: causal attention computes half the scores */
-} srat_layer_desc;
+} srat_layer_desc;               /* limits (SRAT_ERR_INVALID beyond): s, b, h, a < 2^31;
+                                    layers, t < 2^20; n_params < 2^50; s*b*h < 2^60;
+                                    a*s*s*b < 2^70 */
 
 typedef struct {
   int64_t layers_none, layers_selective, layers_full;   /* sum = desc->layers */

@@ -47,15 +47,15 @@ bool check(const srat_layer_desc* d, std::string* err) {
     *err = "sequence_parallel and causal must be 0 or 1";
     return false;
   }
-  // keep every product below 2^120: each factor below 2^40 and at most three
-  // such factors in any product
-  const int64_t lim = (int64_t)1 << 40;
-  if (d->s >= lim || d->b >= lim || d->h >= lim || d->a >= lim || d->layers >= lim || d->t >= lim ||
-      d->n_params >= ((int64_t)1 << 60)) {
-    *err = "sizes out of range";
-    return false;
-  }
-  if ((i128)d->s * d->s * d->a * d->b >= ((i128)1 << 80) || (i128)d->s * d->b * d->h >= ((i128)1 << 80)) {
+  // bounds under which no product below overflows 128 bits: with
+  // s, b, h, a < 2^31, layers, t < 2^20, N < 2^50, sbh < 2^60 and as^2b < 2^70,
+  // a layer's bytes times t stay below 2^85 and times the layer count below
+  // 2^105; A = 4sh < 2^64, so the extra FLOPs (times L) stay below 2^105 and
+  // the base L (6N + 3LA) below 2^127
+  const int64_t lim = (int64_t)1 << 31;
+  if (d->s >= lim || d->b >= lim || d->h >= lim || d->a >= lim || d->layers >= ((int64_t)1 << 20) ||
+      d->t >= ((int64_t)1 << 20) || d->n_params >= ((int64_t)1 << 50) ||
+      (i128)d->s * d->b * d->h >= ((i128)1 << 60) || (i128)d->s * d->s * d->a * d->b >= ((i128)1 << 70)) {
     *err = "sizes out of range";
     return false;
   }
@@ -106,8 +106,8 @@ int plan_recompute(const srat_layer_desc* d, double budget, srat_recompute_plan*
   const i128 L = g.layers;
   const i128 mn = g.mem_t[SRAT_RECOMPUTE_NONE], ms = g.mem_t[SRAT_RECOMPUTE_SELECTIVE],
              mf = g.mem_t[SRAT_RECOMPUTE_FULL];
-  // stored bytes * t must not exceed budget * t; the largest possible need is
-  // below 2^120, so larger budgets are "everything fits"
+  // stored bytes * t must not exceed budget * t; every need is below 2^105,
+  // so larger budgets are "everything fits"
   const long double bt = std::floor((long double)budget * (long double)g.t);
   const i128 cap = bt >= 1e36L ? ((i128)1 << 120) : (i128)bt;
 

@@ -73,7 +73,8 @@ def test_budget_below_full_is_refused_and_plan_zeroed(L):
 
 
 @pytest.mark.parametrize("bad", [dict(s=0), dict(h=-1), dict(layers=0), dict(t=0), dict(n_params=-5),
-                                 dict(a=0), dict(s=1 << 41)])
+                                 dict(a=0), dict(s=1 << 41), dict(layers=1 << 20), dict(t=1 << 20),
+                                 dict(s=1 << 30, b=1 << 30, h=1)])
 def test_invalid_layer_desc(bad):
     kw = dict(s=1024, b=1, h=1024, a=8, layers=4)
     kw.update(bad)
