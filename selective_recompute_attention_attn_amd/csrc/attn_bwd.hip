@@ -34,10 +34,11 @@
 //         (the most queries) are launched first; where two workgroups share
 //         a CU, the grid's second half runs in the mirrored order so that
 //         each pair carries about the same work.
-//   kv_sum: grouped-query attention or split key blocks: dK, dV = sums, in a
-//         fixed order, of the fp32 partials of the q-heads that share a
-//         kv-head and of the two halves of a split block.
-//   dq_sum: split query tiles: dQ = the sum of the two halves' fp32 partials.
+//   sums (one launch after dK/dV, where needed): grouped-query attention or
+//         split key blocks: dK, dV = sums, in a fixed order, of the fp32
+//         partials of the q-heads that share a kv-head and of the two halves
+//         of a split block; split query tiles: dQ = the sum of the two
+//         halves' fp32 partials.
 #include <algorithm>
 #include <type_traits>
 
@@ -744,9 +745,8 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
 // block (slot 1, keys below 128 * split_kb), in a fixed order; written as
 // bf16 in 8-element chunks.  Keys [0, nkeys) are covered.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnParams p, int nkeys) {
+__device__ __forceinline__ void kv_sum_job(const AttnParams& p, int nkeys, int64_t x) {
   const int64_t nk = (int64_t)p.b * nkeys * p.hkv * (D / 8);
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= 2 * nk) return;
   const bool is_v = x >= nk;
   const int64_t y = is_v ? x - nk : x;
@@ -778,10 +778,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnParams p, int 
 
 // dQ of the queries of split tiles (rows from q_lo) = (part 0 + part 1) * scale.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_sum_kernel(AttnParams p, int q_lo) {
+__device__ __forceinline__ void dq_sum_job(const AttnParams& p, int q_lo, int64_t x) {
   const int nrows = p.s - q_lo;
   const int64_t n = (int64_t)p.b * p.hq * nrows * (D / 8);
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= n) return;
   const int c8 = (int)(x % (D / 8));
   const int64_t r = x / (D / 8);                             // (b, hq, query)
@@ -803,6 +802,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_sum_kernel(AttnParams p, int 
   *reinterpret_cast<uint4*>(dst + 8 * c8) = w;
 }
 
+// The partial sums of one backward pass in one launch (after the dK/dV
+// kernel): workgroups [0, dq_blocks) sum the dQ halves of split query tiles
+// (q_lo >= 0), the rest the dK/dV partials of keys [0, nkeys) (nkeys > 0).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_sums_kernel(AttnParams p, int q_lo, int nkeys, int dq_blocks) {
+  const int blk = (int)blockIdx.x;
+  if (blk < dq_blocks) dq_sum_job<D>(p, q_lo, (int64_t)blk * 256 + threadIdx.x);
+  else kv_sum_job<D>(p, nkeys, (int64_t)(blk - dq_blocks) * 256 + threadIdx.x);
+}
+
 template <int D, bool CAUSAL, bool DROP, bool VARLEN>
 hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   const bool part = p.hq != p.hkv;
@@ -811,14 +820,6 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
     TraceScope ts("attn_bwd_dq", st);
     const unsigned nqt = (unsigned)((p.s + kQM - 1) / kQM);
     attn_bwd_dq_kernel<D, CAUSAL, DROP, VARLEN><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.split_qt > 0) {
-    TraceScope ts("attn_bwd_dq_sum", st);
-    const int q_lo = (int)(((p.s + kQM - 1) / kQM - p.split_qt) * kQM);
-    const int64_t n = (int64_t)p.b * p.hq * (p.s - q_lo) * (D / 8);
-    attn_bwd_dq_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, q_lo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -832,11 +833,17 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (!part && p.split_kb == 0) return hipSuccess;
-  TraceScope ts("attn_bwd_kv_sum", st);
+  // partial sums, one launch: dQ of split query tiles, dK/dV of grouped
+  // query heads or of split key blocks
+  const int q_lo = p.split_qt > 0 ? (int)(((p.s + kQM - 1) / kQM - p.split_qt) * kQM) : -1;
+  const int64_t n_dq = q_lo >= 0 ? (int64_t)p.b * p.hq * (p.s - q_lo) * (D / 8) : 0;
   const int nkeys = part ? p.s : min(p.s, 128 * p.split_kb);
-  const int64_t n = 2 * (int64_t)p.b * nkeys * p.hkv * (D / 8);
-  attn_bwd_kv_sum_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, nkeys);
+  const int64_t n_kv = nkeys > 0 ? 2 * (int64_t)p.b * nkeys * p.hkv * (D / 8) : 0;
+  if (n_dq == 0 && n_kv == 0) return hipSuccess;
+  TraceScope ts("attn_bwd_sums", st);
+  const int dq_blocks = (int)((n_dq + 255) / 256);
+  const int kv_blocks = (int)((n_kv + 255) / 256);
+  attn_bwd_sums_kernel<D><<<(unsigned)(dq_blocks + kv_blocks), 256, 0, st>>>(p, q_lo, nkeys, dq_blocks);
   return hipGetLastError();
 }
 

@@ -39,8 +39,7 @@ KERNEL_SOURCES = {
     "attn_fwd_bf16": [CSRC + "attn_fwd.hip"] + _COMMON,
     "attn_bwd_dkdv": _BWD,
     "attn_bwd_dq": _BWD,
-    "attn_bwd_kv_sum": _BWD,
-    "attn_bwd_dq_sum": _BWD,
+    "attn_bwd_sums": _BWD,
     "attn_fwd_merge": [CSRC + "attn_fwd.hip"] + _COMMON,
     "sp_norm_fwd": _NORM,
     "sp_norm_bwd": _NORM,
