@@ -33,6 +33,8 @@
  *               element j takes value j mod 8 (word (j mod 8) div 2, half
  *               (j mod 2)); keep iff value >= T, T = floor(p * 65536 + 0.5)
  *               with p the float drop probability evaluated in double.
+ *               T must stay below 65536: a p that rounds to 65536 (p at or
+ *               above 1 - 2^-17) is refused with SRAT_ERR_INVALID.
  *   scaling   : kept elements are multiplied by 1 / (1 - p) (inverted dropout).
  *
  * Conventions for every call.
@@ -94,8 +96,8 @@ typedef struct {
   int64_t k_stride[3];    /* ... of K, dK */
   int64_t v_stride[3];    /* ... of V, dV */
   int64_t o_stride[3];    /* ... of O, dO */
-  float scale;            /* softmax scale > 0, normally 1/sqrt(d) */
-  float p_drop;           /* attention-dropout probability in [0, 1); 0 disables it */
+  float scale;            /* softmax scale > 0, or 0 for the default 1/sqrt(d) (rounded to float) */
+  float p_drop;           /* attention-dropout probability in [0, 1 - 2^-17); 0 disables it */
   uint64_t seed;          /* Philox key of the attention dropout */
   int64_t head_offset;    /* global index of local q-head 0 (TP rank * hq) */
   const int32_t* seqlens; /* NULL, or device pointer to b valid lengths (int32, 4-byte aligned) */
@@ -162,10 +164,11 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
 typedef struct {
   int32_t dtype;          /* SRAT_BF16 or SRAT_F32 for resid, y, h, u, du, dres, dh, dy */
   int32_t norm;           /* SRAT_LAYERNORM or SRAT_RMSNORM */
-  int64_t s_local, b, h;  /* h % 8 == 0, h <= 32768 */
+  int64_t s_local, b, h;  /* h % 8 == 0, h <= 32768; rows s_local * b below about
+                             2^32 / (threads per row workgroup) (SRAT_ERR_UNSUPPORTED) */
   int64_t seq_offset;     /* global sequence index of local row 0 (SP rank * s_local) */
   float eps;              /* normaliser epsilon, e.g. 1e-5 */
-  float p_drop;           /* hidden-dropout probability in [0, 1) */
+  float p_drop;           /* hidden-dropout probability in [0, 1 - 2^-17) */
   uint64_t seed;          /* Philox key of the hidden dropout */
   int32_t site;           /* which dropout of the layer, 0..127 (e.g. 1 attention, 2 MLP) */
 } srat_norm_desc;
@@ -229,10 +232,9 @@ int srat_trace_read(srat_trace_entry* out, int cap, int reset);
  * planner that picks, layer by layer, what to keep and what to recompute.
  * Host-only (no HIP call, no device pointer).
  *
- * Stored activation bytes of one layer, 2-byte activations ("Recomputing
- * Activations" plate, "What you will learn": 34d + 5HT bytes per token per
- * layer with nothing recomputed, 34d with the attention scores recomputed,
- * 2d with only each layer's input kept):
+ * Stored activation bytes of one layer, 2-byte activations (the per-token
+ * byte formula of the "Recomputing Activations" plate, "What you will learn",
+ * multiplied out per layer):
  *   SRAT_RECOMPUTE_NONE       sbh(34 + 5as/h)
  *   SRAT_RECOMPUTE_SELECTIVE  34sbh        (the attention core is recomputed,
  *                                           what srat_attn_core_bwd does)
@@ -246,8 +248,9 @@ int srat_trace_read(srat_trace_entry* out, int cap, int reset);
  *
  * Extra compute, per token over the layers described: selective re-does the
  * attention-score FLOPs of the forward pass, A = 4sh per layer (2sh causal);
- * full re-does the whole forward pass of the layer, 2N/L + A (training goes
- * from about 6N to 8N FLOPs per token, the plate's second paragraph).  The
+ * full re-does the whole forward pass of the layer, 2N/L + A (one more
+ * forward pass, about a third more training FLOPs: the plate's second
+ * paragraph).  The
  * base is the training FLOPs 6N + 3LA (forward plus backward of the weights
  * and of the attention scores).  All of it divides by t, so the fractions do
  * not depend on t.

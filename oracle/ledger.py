@@ -6,8 +6,9 @@ Bytes of stored activations per layer for sequence length s, micro-batch b,
 hidden size h, a attention heads and tensor-parallel size t (2-byte
 activations):
 
-* no recomputation:          sbh (34 + 5 a s / h)   -- per token "34 d + 5 H T"
-  ("Recomputing Activations" plate, "What you will learn")
+* no recomputation:          sbh (34 + 5 a s / h)   -- the plate's per-token
+  byte formula ("Recomputing Activations" plate, "What you will learn")
+  multiplied by s b
 * selective recomputation:   34 sbh                  (attention scores re-done)
 * full recomputation:        2 sbh                   (each layer's input only)
 * tensor parallel only:      sbh (10 + 24/t + 5 a s / (h t)); the layer norms and
@@ -80,7 +81,8 @@ def model_bytes(d: LayerDims, layers: int, mode: str) -> float:
 
 
 def full_recompute_flops_ratio() -> float:
-    """Training goes from about 6N to 8N FLOPs per token with a second forward."""
+    """A second forward pass on top of forward + backward (2N + 4N per token)
+    adds 2N, a third of the training FLOPs."""
     return 8.0 / 6.0
 
 
@@ -96,16 +98,27 @@ def selective_recompute_extra(n_params: float, d: LayerDims, layers: int,
     return fwd / (6.0 * n_params + 3.0 * fwd)
 
 
-def kept_bytes_this_library(s, b, hq, d_head, dtype_bytes=2, norm="layernorm"):
-    """Bytes the attention core and the norm region of this library keep.
+def kept_bytes_this_library(s, b, hq, hkv, d_head, *, norm_rows, hidden, dtype_bytes=2,
+                            norm="layernorm"):
+    """Bytes this library keeps between its forward and backward calls.
 
-    Attention core: Q, K, V, O (dtype) + LSE (fp32 per query row and head).
-    Norm region: h (dtype) + mean/rstd (fp32 per row).  No s^2 term.
+    Attention core of one rank (b sequences of s positions): Q and O at hq
+    heads, K and V at hkv heads (grouped-query attention shares each kv-head
+    among hq / hkv q-heads), all of d_head values in the activation dtype, plus
+    the fp32 logsumexp of every (sequence, q-head, position).
+    Norm region (norm_rows rows of `hidden` values): h = resid + dropout(y) in
+    the activation dtype, plus fp32 mean and rstd per row (rstd only for
+    RMSNorm).  No dropout mask is kept (both are regenerated) and no term
+    grows with s^2.
     """
-    qkvo = 4 * b * s * hq * d_head * dtype_bytes
+    if hq % hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    q_and_o = 2 * b * s * hq * d_head * dtype_bytes
+    k_and_v = 2 * b * s * hkv * d_head * dtype_bytes
     lse = 4 * b * hq * s
-    stats = (8 if norm == "layernorm" else 4) * s * b
-    return qkvo + lse + stats
+    h_kept = norm_rows * hidden * dtype_bytes
+    stats = (8 if norm == "layernorm" else 4) * norm_rows
+    return q_and_o + k_and_v + lse + h_kept + stats
 
 
 # ---- recompute policy: a per-layer choice of none / selective / full ----------

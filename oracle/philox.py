@@ -70,7 +70,12 @@ def drop_threshold(p: float) -> int:
     p32 = float(np.float32(p))
     if not (0.0 <= p32 < 1.0):
         raise ValueError("drop probability must lie in [0, 1)")
-    return int(np.floor(p32 * 65536.0 + 0.5))
+    T = int(np.floor(p32 * 65536.0 + 0.5))
+    # T = 65536 would drop everything, yet no 16-bit value could reach it and
+    # the threshold no longer fits a 16-bit half: such p are refused
+    if T > 0xFFFF:
+        raise ValueError("drop probability rounds to a 16-bit threshold of 65536 (p >= 1 - 2^-17)")
+    return T
 
 
 def _u16_of(words, e):

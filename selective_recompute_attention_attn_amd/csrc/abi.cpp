@@ -63,6 +63,16 @@ TraceState& trace() {
   return t;
 }
 
+// Drop probability: in [0, 1) and with a 16-bit threshold T = round(p 2^16)
+// below 2^16, so that every draw can pass the comparison "value >= T" and the
+// threshold fits the 16-bit halves the kernels compare against.
+int check_p(float p) {
+  if (!(p >= 0.f && p < 1.f)) return fail(SRAT_ERR_INVALID, "p_drop %g not in [0, 1)", p);
+  if (srat::drop_threshold16(p) > 0xFFFFu)
+    return fail(SRAT_ERR_INVALID, "p_drop %.9g rounds to a 16-bit threshold of 65536: use p < 1 - 2^-17", p);
+  return SRAT_OK;
+}
+
 // ----------------------------------------------------------------- attention
 int check_attn(const srat_attn_desc* d) {
   if (!d) return fail(SRAT_ERR_INVALID, "attn desc is NULL");
@@ -78,8 +88,9 @@ int check_attn(const srat_attn_desc* d) {
     return fail(SRAT_ERR_UNSUPPORTED, "size beyond the 32-bit counter ranges");
   if (d->head_offset < 0 || d->head_offset + d->hq > ((int64_t)1 << 31))
     return fail(SRAT_ERR_INVALID, "head_offset out of range");
-  if (!(d->p_drop >= 0.f && d->p_drop < 1.f)) return fail(SRAT_ERR_INVALID, "p_drop %g not in [0, 1)", d->p_drop);
-  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return fail(SRAT_ERR_INVALID, "scale must be finite and > 0");
+  if (int e = check_p(d->p_drop)) return e;
+  if (!std::isfinite(d->scale) || !(d->scale >= 0.f))
+    return fail(SRAT_ERR_INVALID, "scale must be finite and >= 0 (0: 1/sqrt(d))");
   if (d->seqlens && d->dtype != SRAT_BF16)
     return fail(SRAT_ERR_UNSUPPORTED, "per-element sequence lengths need the bf16 path");
   if (d->seqlens && !aligned(d->seqlens, 4)) return fail(SRAT_ERR_INVALID, "seqlens must be 4-byte aligned");
@@ -107,8 +118,9 @@ srat::AttnParams attn_params(const srat_attn_desc* d) {
   p.b = (int32_t)d->b; p.s = (int32_t)d->s; p.hq = (int32_t)d->hq; p.hkv = (int32_t)d->hkv;
   p.d = (int32_t)d->d;
   p.causal = d->causal;
-  p.scale = d->scale;
-  p.scale_log2 = d->scale * 1.4426950408889634f;
+  // scale 0 asks for the default 1/sqrt(d), rounded to float
+  p.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->d));
+  p.scale_log2 = p.scale * 1.4426950408889634f;
   p.inv_keep = 1.0f / (1.0f - d->p_drop);
   p.thresh = srat::drop_threshold16(d->p_drop);
   p.k0 = (uint32_t)(d->seed & 0xFFFFFFFFu);
@@ -156,8 +168,13 @@ int check_norm(const srat_norm_desc* d) {
     return fail(SRAT_ERR_INVALID, "seq_offset out of range");
   if (d->b > ((int64_t)1 << 24)) return fail(SRAT_ERR_UNSUPPORTED, "batch above 2^24");
   if (d->site < 0 || d->site > 127) return fail(SRAT_ERR_INVALID, "site %d not in 0..127", d->site);
-  if (!(d->p_drop >= 0.f && d->p_drop < 1.f)) return fail(SRAT_ERR_INVALID, "p_drop %g not in [0, 1)", d->p_drop);
+  if (int e = check_p(d->p_drop)) return e;
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return fail(SRAT_ERR_INVALID, "eps must be finite and >= 0");
+  // the backward launches one workgroup per row after the column workgroups;
+  // the grid must stay within 2^32 work-items
+  if (d->s_local * d->b > srat::norm_bwd_max_rows(d->h))
+    return fail(SRAT_ERR_UNSUPPORTED, "%lld rows exceed the %lld the backward grid can hold at h = %lld",
+                (long long)(d->s_local * d->b), (long long)srat::norm_bwd_max_rows(d->h), (long long)d->h);
   return SRAT_OK;
 }
 

@@ -48,6 +48,8 @@ struct NormBwdParams {
 };
 
 hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStream_t st);
+// largest row count whose backward grid fits the launch limits, for row width hdim
+int64_t norm_bwd_max_rows(int64_t hdim);
 hipError_t launch_norm_bwd(const NormBwdParams& p, bool bf16, bool rms, hipStream_t st);
 hipError_t launch_hidden_mask(const NormFwdParams& p, uint8_t* mask, hipStream_t st);
 

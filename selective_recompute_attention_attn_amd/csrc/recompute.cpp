@@ -1,18 +1,20 @@
 // Recompute policy: the activation-memory ledger of a transformer layer and
 // the choice, layer by layer, of what to store and what to recompute.
 //
-// Ledger ("Recomputing Activations" plate, "What you will learn"): one layer
-// stores 34d + 5HT bytes per token with nothing recomputed, 34d when the
-// attention scores are recomputed (selective), 2d when only the layer input is
-// kept (full).  Per layer that is sbh(34 + 5as/h), 34sbh and 2sbh.  Under
+// Ledger ("Recomputing Activations" plate, "What you will learn", the
+// per-token byte formula): per layer, sbh(34 + 5as/h) bytes when nothing is
+// recomputed, 34sbh once the attention-score activations are dropped and
+// rebuilt (selective), and 2sbh when a layer keeps nothing but its input
+// (full).  Under
 // tensor parallelism of size t the layer norms and the dropouts after
 // attention and the MLP (10sbh) stay whole on every rank and the rest divides
 // by t; sequence parallelism divides the 10sbh as well (LIT-736 record, Key
 // takeaways bullets 1-2).
 //
-// Compute: a fully recomputed layer runs its forward pass twice (training goes
-// from about 6N to 8N FLOPs per token, the plate's second paragraph); a
-// selectively recomputed one re-does only the attention-score FLOPs.
+// Compute: a fully recomputed layer runs its forward pass a second time, one
+// extra forward on top of forward plus backward, so about a third more
+// training FLOPs (the plate's second paragraph); a selectively recomputed one
+// re-does only the attention-score FLOPs.
 //
 // Every quantity is kept as an exact integer: bytes scaled by t, FLOPs per
 // token scaled by L, so the planner's comparisons have no rounding.

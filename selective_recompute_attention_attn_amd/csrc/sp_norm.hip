@@ -536,6 +536,15 @@ int norm_bwd_col_blocks(int hdim) {
   return 8 * ((nslab + 7) / 8);
 }
 
+// The backward grid is col_blocks + rows workgroups of pick_block(h) threads:
+// it must stay below 2^32 work-items and 2^31 workgroups.
+int64_t norm_bwd_max_rows(int64_t hdim) {
+  if (hdim <= 0 || hdim > 32768) return 0;
+  const int64_t block = pick_block((int)hdim);
+  const int64_t cols = norm_bwd_col_blocks((int)hdim);
+  return std::min<int64_t>((((int64_t)1 << 32) - 1) / block, ((int64_t)1 << 31) - 1) - cols;
+}
+
 hipError_t launch_norm_fwd(const NormFwdParams& p, bool bf16, bool rms, hipStream_t st) {
   if (p.rows == 0) return hipSuccess;
   TraceScope ts("sp_norm_fwd", st);

@@ -9,7 +9,6 @@ fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -146,7 +145,7 @@ def attn_desc(q, k, v, o, *, causal: bool, scale: Optional[float], p_drop: float
         raise SratError("q, k, v, o must share a dtype")
     return AttnDesc(dtype=_dtype_code(q), causal=int(bool(causal)), b=b, s=s, hq=hq, hkv=hkv, d=d,
                     q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o),
-                    scale=float(1.0 / math.sqrt(d) if scale is None else scale), p_drop=float(p_drop),
+                    scale=0.0 if scale is None else float(scale), p_drop=float(p_drop),
                     seed=int(seed) & 0xFFFFFFFFFFFFFFFF, head_offset=int(head_offset),
                     seqlens=None if seqlens is None else _seqlens_ptr(seqlens, b, q.device))
 

@@ -59,8 +59,8 @@ def _err(L, rc):
     (dict(d=48), -2), (dict(d=320), -2), (dict(d=192, dtype=ops.SRAT_F32), -2), (dict(d=256, dtype=ops.SRAT_F32), -2), (dict(p_drop=1.0), -1), (dict(p_drop=-0.1), -1),
     (dict(hq=4, hkv=3), -1), (dict(dtype=7), -1), (dict(causal=2), -1), (dict(s=-1), -1),
     (dict(q_stride=(256 * 4 * 64, 4 * 64, 60)), -1), (dict(k_stride=(0, 3, 64)), -1),
-    (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1), (dict(scale=0.0), -1),
-    (dict(scale=-0.1), -1)])
+    (dict(head_offset=-1), -1), (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1),
+    (dict(scale=-0.1), -1), (dict(p_drop=1.0 - 2.0**-18), -1), (dict(p_drop=0.999995), -1)])
 def test_attention_validation_before_any_hip_call(L, kw, code):
     d = _desc(**kw)
     n = ctypes.c_size_t(0)
@@ -109,7 +109,10 @@ def _ndesc(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(h=100), -2), (dict(h=65536), -2), (dict(norm=3), -1), (dict(p_drop=1.0), -1),
-    (dict(site=200), -1), (dict(b=0), -1), (dict(eps=-1.0), -1), (dict(seq_offset=-5), -1)])
+    (dict(site=200), -1), (dict(b=0), -1), (dict(eps=-1.0), -1), (dict(seq_offset=-5), -1),
+    (dict(p_drop=1.0 - 2.0**-18), -1),
+    # the backward's grid (column workgroups + one per row) must fit 2^32 work-items
+    (dict(h=256, s_local=1 << 26, b=1), -2), (dict(h=6144, s_local=1 << 23, b=2), -2)])
 def test_norm_validation_before_any_hip_call(L, kw, code):
     d = _ndesc(**kw)
     n = ctypes.c_size_t(0)
@@ -169,9 +172,55 @@ def test_library_philox_equals_oracle(philox_hpp):
 
 def test_threshold_rule_matches_oracle():
     # the host code computes T from the float probability in double precision
-    for p in (0.0, 0.1, 0.25, 0.3333, 0.9999):
+    for p in (0.0, 0.1, 0.25, 0.3333, 0.9999, 1.0 - 2.0**-16, 1.0 - 2.0**-17 - 2.0**-24):
         t = int(float(np.float32(p)) * 65536.0 + 0.5)
-        assert t == ph.drop_threshold(p)
+        assert t == ph.drop_threshold(p) and t <= 0xFFFF
+
+
+@pytest.mark.parametrize("p", [1.0 - 2.0**-17, 1.0 - 2.0**-18, 0.999995, float(np.nextafter(np.float32(1), 0))])
+def test_threshold_65536_refused_on_both_sides(L, p):
+    """A p whose 16-bit threshold rounds to 65536 is refused by the oracle and
+    by every entry point (attention and norm descriptors) before any HIP call:
+    the kernels compare 16-bit halves against T and cannot express it."""
+    assert int(float(np.float32(p)) * 65536.0 + 0.5) == 65536
+    with pytest.raises(ValueError):
+        ph.drop_threshold(p)
+    n = ctypes.c_size_t(0)
+    d = _desc(p_drop=p)
+    rc, msg = _err(L, L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)))
+    assert rc == -1 and "65536" in msg
+    nd = _ndesc(p_drop=p)
+    rc, msg = _err(L, L.srat_sp_norm_bwd_workspace(ctypes.byref(nd), ctypes.byref(n)))
+    assert rc == -1 and "65536" in msg
+
+
+def test_scale_zero_means_the_default(L):
+    """scale = 0 asks the library for 1/sqrt(d): the descriptor is valid and
+    the binding passes 0 when no scale is given (the binding computes no part
+    of the method)."""
+    n = ctypes.c_size_t(0)
+    d = _desc(scale=0.0)
+    assert L.srat_attn_core_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    import torch
+    z = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    assert ops.attn_desc(z, z, z, z, causal=True, scale=None, p_drop=0.0, seed=0, head_offset=0).scale == 0.0
+    assert ops.attn_desc(z, z, z, z, causal=True, scale=0.25, p_drop=0.0, seed=0, head_offset=0).scale == 0.25
+
+
+def test_norm_row_limit_boundary(L):
+    """The largest row count the backward grid holds is accepted, one more is not."""
+    n = ctypes.c_size_t(0)
+    for h in (256, 6144, 32768):
+        groups = (h + 7) // 8
+        blk = 64
+        while blk < 1024 and (groups + blk - 1) // blk > 3:
+            blk *= 2
+        cols = 8 * (((h + 31) // 32 + 7) // 8)
+        limit = min((2**32 - 1) // blk, 2**31 - 1) - cols
+        ok = _ndesc(h=h, s_local=limit, b=1)
+        assert L.srat_sp_norm_bwd_workspace(ctypes.byref(ok), ctypes.byref(n)) == 0, (h, L.srat_last_error())
+        bad = _ndesc(h=h, s_local=limit + 1, b=1)
+        assert _err(L, L.srat_sp_norm_bwd_workspace(ctypes.byref(bad), ctypes.byref(n)))[0] == -2
 
 
 def test_seqlens_only_on_the_bf16_path(L):

@@ -35,7 +35,18 @@ def run_both(n: gen.NormShape, x, device, alias_dy=False):
 
 
 def check(got, ref, tol):
-    return {k: assert_close(k, got[k], ref[k], tol) for k in ref}
+    """Per-tensor and per-row max-norm relative errors (rows of h values for h,
+    u, dh, dy; one value per row for the statistics; dgamma and dbeta are
+    per-column sums over all rows, checked per tensor).  A row's mean is a sum
+    of terms h_j / h that can nearly cancel: it is judged against the larger of
+    itself and mean |h_j|, the size of its terms."""
+    def row_len(k):
+        if k in ("mean", "rstd"):
+            return 1
+        return 0 if k in ("dgamma", "dbeta") else np.asarray(ref[k]).shape[-1]
+    h_ref = np.asarray(ref["h"], np.float64)
+    floors = {"mean": np.mean(np.abs(h_ref.reshape(-1, h_ref.shape[-1])), axis=1)}
+    return {k: assert_close(k, got[k], ref[k], tol, row_len=row_len(k), row_floor=floors.get(k)) for k in ref}
 
 
 def test_tiny_fp32_workload():

@@ -88,9 +88,46 @@ def test_each_technique_about_halves_and_together_under_20pct(h, a):
 
 
 def test_this_library_keeps_no_s2_term():
-    a = lg.kept_bytes_this_library(s=2048, b=1, hq=12, d_head=128)
-    b = lg.kept_bytes_this_library(s=4096, b=1, hq=12, d_head=128)
-    assert b == pytest.approx(2 * a)          # linear in s
+    a = lg.kept_bytes_this_library(s=2048, b=1, hq=12, hkv=12, d_head=128, norm_rows=256, hidden=12288)
+    b = lg.kept_bytes_this_library(s=4096, b=1, hq=12, hkv=12, d_head=128, norm_rows=512, hidden=12288)
+    assert b == 2 * a          # linear in s (the norm rows are s/t of them)
+
+
+# Hand-counted totals (bytes), tensor by tensor, for shapes of the workloads:
+#   Llama-3-70B rank (s 8192, b 1, 8 q-heads sharing 1 kv-head of 128, bf16;
+#   RMSNorm region of 1024 rows of 8192):
+#     Q 8192*8*128*2 = 16777216, O the same, K 8192*1*128*2 = 2097152, V the
+#     same, LSE 4*8*8192 = 262144, h 1024*8192*2 = 16777216, rstd 4*1024 = 4096
+#   22B GPT rank (s 2048, b 4, 8 heads of 96 for q and kv, bf16; LayerNorm
+#   region of 1024 rows of 6144):
+#     Q, K, V, O 4*2048*8*96*2 = 12582912 each, LSE 4*4*8*2048 = 262144,
+#     h 1024*6144*2 = 12582912, mean + rstd 8*1024 = 8192
+#   tiny grouped case (s 4, b 1, 2 q-heads on 1 kv-head of 8, fp32; LayerNorm
+#   region of 4 rows of 16):
+#     Q 4*2*8*4 = 256, O 256, K 4*1*8*4 = 128, V 128, LSE 4*2*4 = 32,
+#     h 4*16*4 = 256, mean + rstd 8*4 = 32
+@pytest.mark.parametrize("kw,total", [
+    (dict(s=8192, b=1, hq=8, hkv=1, d_head=128, norm_rows=1024, hidden=8192, norm="rmsnorm"),
+     16777216 * 2 + 2097152 * 2 + 262144 + 16777216 + 4096),
+    (dict(s=2048, b=4, hq=8, hkv=8, d_head=96, norm_rows=1024, hidden=6144),
+     12582912 * 4 + 262144 + 12582912 + 8192),
+    (dict(s=4, b=1, hq=2, hkv=1, d_head=8, norm_rows=4, hidden=16, dtype_bytes=4),
+     256 + 256 + 128 + 128 + 32 + 256 + 32),
+])
+def test_kept_bytes_hand_counted(kw, total):
+    """Pinned to tensor-by-tensor counts: a version that counts K and V at the
+    q-head count (blind to grouped-query sharing) gives 84.2 MB instead of
+    54.8 MB on the Llama shape and 1344 instead of 1088 bytes on the tiny one."""
+    assert lg.kept_bytes_this_library(**kw) == total
+
+
+def test_kept_bytes_gqa_blind_variant_is_caught():
+    """A planted mistake (K and V counted at hq heads) disagrees with the pin."""
+    kw = dict(s=8192, b=1, hq=8, hkv=1, d_head=128, norm_rows=1024, hidden=8192, norm="rmsnorm")
+    blind = dict(kw, hkv=8)
+    assert lg.kept_bytes_this_library(**blind) != 16777216 * 2 + 2097152 * 2 + 262144 + 16777216 + 4096
+    with pytest.raises(ValueError):
+        lg.kept_bytes_this_library(**dict(kw, hkv=3))
 
 
 # ---- the recompute-policy planner (a per-layer choice of none / selective / full)
