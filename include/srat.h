@@ -158,6 +158,29 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
                        void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward as srat_attn_core_bwd, with its workspace taken from a scratch
+ * array of SRAT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on from the moment its code is loaded until the process ends.  The
+ * call allocates nothing and calls no allocating routine.
+ *   - Shapes whose srat_attn_core_bwd_workspace() exceeds
+ *     SRAT_NOALLOC_SCRATCH_BYTES are refused with SRAT_ERR_UNSUPPORTED, before
+ *     any HIP call.
+ *   - The scratch is found on the device current at the call, which must be
+ *     the device of `stream` and of the tensors.
+ *   - Every call on one GPU shares that GPU's scratch and leaves its contents
+ *     behind; the kernels write every scratch byte before they read it, so no
+ *     clearing is needed.  Calls whose execution overlaps on one GPU (several
+ *     streams or threads) race on the scratch: serialise them.
+ * Arguments, layouts, outputs and errors otherwise as srat_attn_core_bwd.
+ */
+#define SRAT_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int srat_attn_core_bwd_noalloc(const srat_attn_desc* desc, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* stream);
+
+/*
  * Sequence-parallel norm region of one rank: rows [s_local, b, h], contiguous,
  * h contiguous; row (sl, bb) is global sequence position seq_offset + sl.
  */

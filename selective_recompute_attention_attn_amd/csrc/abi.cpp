@@ -224,6 +224,49 @@ int attn_fwd_impl(const srat_attn_desc* desc, const void* q, const void* k, cons
   return SRAT_OK;
 }
 
+int check_bwd_tensors(const srat_attn_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, const void* dq, const void* dk, const void* dv) {
+  if (desc->b * desc->s == 0) return SRAT_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(SRAT_ERR_INVALID, "NULL tensor pointer");
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned(ptr, 16)) return fail(SRAT_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(SRAT_ERR_INVALID, "lse must be 4-byte aligned");
+  return SRAT_OK;
+}
+
+int attn_bwd_launch(const srat_attn_desc* desc, const AttnWs& w, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                    void* stream);
+
+// ---- scratch of the allocation-free backward entry point.  One array per
+// GPU, reserved when the code object is loaded and held until the process
+// ends.  In host code the array's name is only a stand-in: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = SRAT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_ptr(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;   // device ordinal -> address of its copy of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(SRAT_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return SRAT_OK;
+}
+
 }  // namespace
 
 namespace srat {
@@ -292,17 +335,39 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
                        size_t ws_bytes, void* stream) {
   g_err.clear();
   if (int e = check_attn(desc)) return e;
+  if (int e = check_bwd_tensors(desc, q, k, v, o, lse, dout, dq, dk, dv)) return e;
   const AttnWs w = attn_ws(desc);
   if (desc->b * desc->s > 0) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
-      return fail(SRAT_ERR_INVALID, "NULL tensor pointer");
-    const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
-    for (const void* ptr : ptrs)
-      if (!aligned(ptr, 16)) return fail(SRAT_ERR_INVALID, "tensor pointers must be 16-byte aligned");
     if (!ws || ws_bytes < w.total)
       return fail(SRAT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
     if (!aligned(ws, 256)) return fail(SRAT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
+  return attn_bwd_launch(desc, w, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+}
+
+int srat_attn_core_bwd_noalloc(const srat_attn_desc* desc, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* stream) {
+  g_err.clear();
+  if (int e = check_attn(desc)) return e;
+  if (int e = check_bwd_tensors(desc, q, k, v, o, lse, dout, dq, dk, dv)) return e;
+  const AttnWs w = attn_ws(desc);
+  if (w.total > kScratchBytes)
+    return fail(SRAT_ERR_UNSUPPORTED, "this shape needs %zu bytes of workspace; the no-allocation entry point "
+                "has %zu (use srat_attn_core_bwd with a caller workspace)", w.total, kScratchBytes);
+  if (desc->b * desc->s == 0) return SRAT_OK;
+  void* ws = nullptr;
+  if (int e = scratch_ptr(&ws)) return e;
+  return attn_bwd_launch(desc, w, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attn_bwd_launch(const srat_attn_desc* desc, const AttnWs& w, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                    void* stream) {
   srat::AttnParams p = attn_params(desc);
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.dout = dout;
   p.dq = dq; p.dk = dk; p.dv = dv;
@@ -319,6 +384,10 @@ int srat_attn_core_bwd(const srat_attn_desc* desc, const void* q, const void* k,
   if (e != hipSuccess) return hip_fail(e, "attn_core_bwd launch");
   return SRAT_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int srat_sp_norm_bwd_workspace(const srat_norm_desc* desc, size_t* bytes) {
   g_err.clear();

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libsrat.so")
 SRAT_F32, SRAT_BF16 = 1, 2
 SRAT_LAYERNORM, SRAT_RMSNORM = 1, 2
 ERRORS = {-1: "SRAT_ERR_INVALID", -2: "SRAT_ERR_UNSUPPORTED", -3: "SRAT_ERR_WORKSPACE", -4: "SRAT_ERR_HIP"}
-EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_fwd_workspace", "srat_attn_core_fwd_ws", "srat_attn_core_bwd", "srat_attn_core_bwd_workspace", "srat_sp_norm_fwd",
+EXPORTS = ("srat_attn_core_fwd", "srat_attn_core_fwd_workspace", "srat_attn_core_fwd_ws", "srat_attn_core_bwd",
+           "srat_attn_core_bwd_workspace", "srat_attn_core_bwd_noalloc", "srat_sp_norm_fwd",
            "srat_sp_norm_bwd", "srat_sp_norm_bwd_workspace", "srat_dropout_mask_dump", "srat_trace_enable",
            "srat_trace_read", "srat_last_error", "srat_version", "srat_activation_bytes",
            "srat_plan_recompute")
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.srat_attn_core_fwd_ws.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, sz, vp]
         L.srat_attn_core_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.srat_attn_core_bwd_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
+        L.srat_attn_core_bwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.srat_sp_norm_fwd.argtypes = [ctypes.POINTER(NormDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.srat_sp_norm_bwd.argtypes = [ctypes.POINTER(NormDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.srat_sp_norm_bwd_workspace.argtypes = [ctypes.POINTER(NormDesc), ctypes.POINTER(sz)]
@@ -267,6 +269,24 @@ def attn_core_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optiona
     prepare_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=causal, scale=scale, p_drop=p_drop,
                      seed=seed, head_offset=head_offset, seqlens=seqlens)()
     return dq, dk, dv
+
+
+def attn_core_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, causal: bool = False,
+                          scale: Optional[float] = None, p_drop: float = 0.0, seed: int = 0, head_offset: int = 0,
+                          seqlens: Optional[torch.Tensor] = None, stream=None) -> None:
+    """srat_attn_core_bwd_noalloc into preallocated dq, dk, dv (strides of q, k,
+    v): the backward with the library's own scratch, no workspace argument."""
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise SratError("dout must have o's shape and strides")
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise SratError("preallocated gradients must match q, k, v")
+    desc = attn_desc(q, k, v, o, causal=causal, scale=scale, p_drop=p_drop, seed=seed, head_offset=head_offset,
+                     seqlens=seqlens)
+    _check(lib().srat_attn_core_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                            _stream_arg(q.device, stream)),
+           "srat_attn_core_bwd_noalloc")
 
 
 def norm_desc(x: torch.Tensor, *, norm: str, eps: float, p_drop: float, seed: int, site: int,

@@ -84,6 +84,29 @@ def test_null_descriptor_and_null_pointers(L):
     assert rc == -3 and "workspace" in msg
 
 
+def test_noalloc_backward_refuses_oversized_shapes_before_any_hip_call(L):
+    """The allocation-free backward takes its workspace from a fixed scratch
+    array: a shape needing more is refused with SRAT_ERR_UNSUPPORTED, and bad
+    descriptors and pointers are refused as by srat_attn_core_bwd, all before
+    any HIP call (so on a machine without a GPU)."""
+    limit = 128 << 20
+    fake = [ctypes.c_void_p(0x10000)] * 9
+    hq, d = 8, 128
+    for s, ok in ((8192, True), (32768, False)):
+        qs, ks = (s * hq * d, hq * d, d), (s * d, d, d)
+        desc = _desc(s=s, hq=hq, hkv=1, d=d, q_stride=qs, o_stride=qs, k_stride=ks, v_stride=ks)
+        n = ctypes.c_size_t(0)
+        assert L.srat_attn_core_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)) == 0
+        assert (n.value <= limit) == ok
+        if not ok:
+            rc, msg = _err(L, L.srat_attn_core_bwd_noalloc(ctypes.byref(desc), *fake, None))
+            assert rc == -2 and "no-allocation" in msg and str(limit) in msg
+    rc, msg = _err(L, L.srat_attn_core_bwd_noalloc(ctypes.byref(_desc()), *([None] * 9), None))
+    assert rc == -1 and "NULL" in msg
+    rc, _ = _err(L, L.srat_attn_core_bwd_noalloc(ctypes.byref(_desc(d=48)), *fake, None))
+    assert rc == -2
+
+
 def test_workspace_is_linear_in_s_never_quadratic(L):
     """The backward workspace holds per-row data only: D (4 bytes per query
     row) plus, for grouped-query heads or split grids, at most two fp32 slots
