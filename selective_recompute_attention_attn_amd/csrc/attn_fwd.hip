@@ -429,6 +429,349 @@ __global__ __launch_bounds__(kThreads, fwd_occupancy<D>()) void attn_fwd_bf16_ke
   }
 }
 
+// ---------------------------------------------------------------- ping-pong
+// The same forward with two waves on every SIMD, paired so that one wave's
+// softmax (VALU) runs while the other's matrix products (MFMA) run.
+//
+// A workgroup has 8 waves in two groups of 4 over the same 128 queries (wave
+// w of either group owns queries 32w .. 32w+31).  Group g takes the key tiles
+// kt_lo + 2j + g (j = 0, 1, ...): each group keeps its own running max, row
+// sum and O accumulator, and the two are merged through LDS at the end (the
+// same exact combination as a split tile's merge).
+//
+// Each group alternates two barrier-separated phases per tile:
+//   M(j): O^T += V[j-1]^T P[j-1]^T  and  S[j]^T = K[j] Q^T   (MFMA)
+//   V(j): stage the group's next K/V tile into LDS, start the loads of the one
+//         after; row max, rare rescale, exp, row sum, dropout, pack P[j] (VALU)
+// and group 1 runs one phase behind group 0, so that in every interval between
+// two barriers one group issues MFMAs and the other VALU work.  Row sums are
+// taken from the packed bf16 probabilities with v_dot2c_f32_bf16 (two per
+// instruction), the values the PV product uses.
+template <int D>
+struct alignas(16) FwdPPSmem {
+  static constexpr int kKS = RowStride<D>::kValue;
+  static constexpr int kVS = TileStride<D>::kValue;
+  union {
+    struct {
+      bf16 k[2][2][kBN * kKS];   // [group][buffer]: K rows in slot order
+      bf16 v[2][2][kBN * kVS];   // V rows (read transposed)
+    } t;
+    struct {                     // group 1's state handed to group 0
+      float o[4][(D / 32) * 16][64];
+      float m[4][64];
+      float l[4][64];
+    } x;
+  };
+};
+
+__device__ __forceinline__ float dot2_sum(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+}
+
+template <int D, bool CAUSAL, bool DROP, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
+  using SM = FwdPPSmem<D>;
+  constexpr int kKS = SM::kKS;
+  constexpr int kVS = SM::kVS;
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kLoads = D / 32;     // 16-byte loads per thread per 64 x D tile (a group's 256 threads)
+  __shared__ SM sm;
+
+  const int nqt = (p.s + kBM - 1) / kBM;
+  const int nbh = p.b * p.hq;
+  const int bh = blockIdx.x % nbh;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int nsq = kSplitFwd<D, CAUSAL> ? p.split_qt : 0;
+  int qt, part = -1;
+  if (nsq > 0) {
+    split_order(rank, nqt, nsq, qt, part);
+  } else {
+    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  }
+  const int hh_q = bh % p.hq;
+  const int bb = bh / p.hq;
+  const int g = hh_q / (p.hq / p.hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
+  const int grp = wv >> 2, wq = wv & 3;                       // key group, query block
+  const int gtid = tid & 255;                                 // thread within the group
+  const int half = lane >> 5, col = lane & 31;
+  const int q0 = qt * kBM;
+  const int qw = q0 + 32 * wq;
+  const int qi = qw + col;
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;
+
+  const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
+  const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
+  const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
+
+  if (VARLEN && q0 >= sl) {   // a tile past the valid length: O = 0, LSE = -inf
+    if (grp == 0 && qi < p.s) {
+      const int64_t row = ((int64_t)bb * p.hq + hh_q) * p.s + qi;
+      if (part >= 0) {
+        const int64_t prow = (int64_t)part * p.b * p.hq * p.s + row;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j)
+          if (j % 2 == half) *reinterpret_cast<float4*>(p.o_part + prow * D + 4 * j) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (half == 0) p.lse_part[prow] = -INFINITY;
+      } else {
+        bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c)
+          if (c % 2 == half) *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(0, 0, 0, 0);
+        if (half == 0) p.lse_out[row] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  bf16x8 qreg[kDC];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) qreg[c] = bf16x8{};
+  if (qi < sl) {
+#pragma unroll
+    for (int c = 0; c < kDC; ++c)
+      qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
+  }
+
+  f32x16 oacc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) oacc[db] = f32x16{};
+  float m_use = -INFINITY;
+  float l_run = 0.f;
+
+  const int nkt_all = (sl + kBN - 1) / kBN;
+  const int nkt_q = CAUSAL ? min(nkt_all, (q0 + kBM + kBN - 1) / kBN) : nkt_all;
+  const int kt_mid = (nkt_q + 1) / 2;
+  const int kt_lo = part == 1 ? kt_mid : 0;
+  const int nkt = part == 0 ? kt_mid : nkt_q;
+  const int nsteps = (nkt - kt_lo + 1) / 2;                       // steps of both groups
+  const int n_int = CAUSAL ? min(sl / kBN, (qw + 1) / kBN) : sl / kBN;
+  const int key_lim = CAUSAL ? min(sl, qi + 1) : sl;
+  auto tile_of = [&](int j) { return kt_lo + 2 * j + grp; };
+
+  // ---- staging of the group's tiles (chunk x = gtid + 256 it of a 64 x D tile)
+  uint4 kpre[kLoads], vpre[kLoads];
+  uint32_t koff[kLoads], voff[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int x = gtid + 256 * it;
+    koff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sk_s + 8 * (x % (D / 8))) * 2);
+    voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
+  }
+  auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
+    const int rows = kt < nkt ? min(kBN, max(0, sl - kt * kBN)) : 0;
+    return (uint32_t)((int64_t)rows * stride * 2);
+  };
+  auto load_kv = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp + (int64_t)kt * kBN * p.sk_s, tile_bytes(kt, p.sk_s));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + (int64_t)kt * kBN * p.sv_s, tile_bytes(kt, p.sv_s));
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      kpre[it] = buffer_load16(rk, koff[it]);
+      vpre[it] = buffer_load16(rv, voff[it]);
+    }
+  };
+  auto stash_kv = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int x = gtid + 256 * it;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<uint4*>(&sm.t.k[grp][buf][((r & ~31) | slot32(r & 31)) * kKS + 8 * c8]) = kpre[it];
+      *reinterpret_cast<uint4*>(&sm.t.v[grp][buf][r * kVS + 8 * c8]) = vpre[it];
+    }
+  };
+
+  const int krow = col * kKS + 8 * half;
+  const int lgp = lane >> 4, lg = lane & 15;
+  const int vrow = (16 * (lgp >> 1) + (lg >> 2)) * kVS + 16 * (lgp & 1) + 4 * (lg & 3);
+  auto v_operand = [&](const bf16* vb, int c, int db) -> bf16x8 {
+    const int r0 = (32 * (c >> 1) + 8 * (c & 1)) * kVS + vrow;
+    const s16x4 lo = lds_read_tr16(&vb[r0 + 32 * db]);
+    const s16x4 hi = lds_read_tr16(&vb[r0 + 4 * kVS + 32 * db]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const PhiloxRow prow = philox_row((uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+  const uint32_t tm1 = (p.thresh - 1u) * 0x10001u;
+  const float c2 = p.scale_log2;
+
+  f32x16 s[2];        // S^T of the current tile (raw scores)
+  uint32_t pw[16];    // P^T of the previous tile, packed bf16 pairs
+
+  // M phase of step j: PV of step j-1 (if it had a tile), QK^T of step j
+  auto phase_m = [&](int j, bool pv, bool qk) {
+    if (pv) {
+      const bf16* vb = sm.t.v[grp][(j - 1) & 1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 pop =
+            __builtin_bit_cast(bf16x8, make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) oacc[db] = mfma32(v_operand(vb, c, db), pop, oacc[db]);
+      }
+    }
+    if (qk) {
+      const bf16* kb_ = sm.t.k[grp][j & 1];
+      s[0] = s[1] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&kb_[32 * kb * kKS + krow + 16 * c]), qreg[c], s[kb]);
+    }
+  };
+
+  // V phase of step j: stage the group's tile of step j+1, load step j+2;
+  // softmax of step j's scores into pw (MASK: causal / tail masking needed)
+  auto phase_v = [&](int j, bool have, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    stash_kv((j + 1) & 1);
+    load_kv(tile_of(j + 2));
+    if (!have) return;
+    const int key0 = tile_of(j) * kBN;
+    uint32_t w[16];
+    if (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {
+          const Philox4 rnd = philox4x32_10_row((uint32_t)((key0 + 32 * kb + 16 * half + 8 * gh) >> 3), prow);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) w[8 * kb + 4 * gh + jj] = rnd.w[jj];
+        }
+    }
+    if (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 16 * half + r;
+          s[kb][r] = key >= key_lim ? -INFINITY : s[kb][r];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = halves_max(mx) * c2;
+    const bool grow = mx > m_use + kMaxSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_use;
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
+      m_use = m_new;
+    }
+    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -msub));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c2, -msub));
+        uint32_t pk = pack_bf16x2(e0, e1);
+        l_run = dot2_sum(pk, l_run);
+        if (DROP) pk = drop_pair(pk, w[8 * kb + (r >> 1)], tm1);
+        pw[8 * kb + (r >> 1)] = pk;
+      }
+  };
+
+  // ---- prologue: the group's step-0 tile resident, step 1 in flight
+  load_kv(tile_of(0));
+  stash_kv(0);
+  load_kv(tile_of(1));
+  __syncthreads();
+  if (grp == 1) __syncthreads();   // group 1 runs one phase behind
+
+  // steps whose tile needs no masking for this wave: tile_of(j) < n_int
+  const int j_int = max(0, min(nsteps, (min(n_int, nkt) - kt_lo - grp + 1) / 2));
+  int j = 0;
+  for (; j < j_int; ++j) {
+    phase_m(j, j > 0, true);
+    __syncthreads();
+    phase_v(j, true, bool_c<false>{});
+    __syncthreads();
+  }
+  for (; j < nsteps; ++j) {
+    const bool have = tile_of(j) < nkt;
+    phase_m(j, j > 0, have);
+    __syncthreads();
+    phase_v(j, have, bool_c<true>{});
+    __syncthreads();
+  }
+  phase_m(nsteps, nsteps > 0 && tile_of(nsteps - 1) < nkt, false);
+  __syncthreads();
+  if (grp == 0) __syncthreads();   // balances group 1's extra barrier
+
+  // ---- merge group 1 into group 0 (both over the same queries)
+  l_run = halves_sum(l_run);
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.x.o[wq][db * 16 + r][lane] = oacc[db][r];
+    sm.x.m[wq][lane] = m_use;
+    sm.x.l[wq][lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = sm.x.m[wq][lane], l1 = sm.x.l[wq][lane];
+    const float mm = fmaxf(m_use, m1);
+    const float a0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_use - mm);
+    const float a1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + sm.x.o[wq][db * 16 + r][lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_use = mm;
+  }
+
+  // ---- epilogue (as the one-group kernel): O = O^T / l * 1/(1-p), LSE
+  const float l_tot = l_run;
+  if (part >= 0) {
+    if (qi < p.s) {
+      const int64_t row = (int64_t)part * p.b * p.hq * p.s + ((int64_t)bb * p.hq + hh_q) * p.s + qi;
+      const bool any = l_tot > 0.f && (!VARLEN || qi < sl);
+      const float inv = any ? 1.0f / l_tot : 0.f;
+      float* dst = p.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * half) =
+              make_float4(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
+                          oacc[db][4 * a + 3] * inv);
+      if (half == 0) p.lse_part[row] = any ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  if (qi < p.s) {
+    const bool valid = !VARLEN || qi < sl;
+    const float inv = valid ? p.inv_keep / l_tot : 0.f;
+    bf16* op = static_cast<bf16*>(p.out) + bb * p.so_b + (int64_t)qi * p.so_s + hh_q * p.so_h;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 w2;
+        w2.x = pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv);
+        w2.y = pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * a + 4 * half) = w2;
+      }
+    }
+    if (half == 0)
+      p.lse_out[((int64_t)bb * p.hq + hh_q) * p.s + qi] = valid ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // Merge of the two parts of a split tile's rows (from q_lo): LSE =
 // log(e^LSE0 + e^LSE1), O = (e^(LSE0-LSE) O0 + e^(LSE1-LSE) O1) / (1-p).
 template <int D>
@@ -464,6 +807,10 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(AttnParams p, int q
   if (c8 == 0) p.lse_out[row] = lse;
 }
 
+// head dims whose forward runs as the ping-pong kernel (8 waves)
+template <int D>
+constexpr bool kFwdPingPong = D == 128;
+
 template <int D, bool VARLEN>
 hipError_t fwd_launch_v(const AttnParams& p, hipStream_t st) {
   const int nqt = (p.s + kBM - 1) / kBM;
@@ -471,7 +818,15 @@ hipError_t fwd_launch_v(const AttnParams& p, hipStream_t st) {
   const bool drop = p.thresh != 0;
   {
     TraceScope ts("attn_fwd_bf16", st);
-    if (p.causal) {
+    if constexpr (kFwdPingPong<D>) {
+      if (p.causal) {
+        if (drop) attn_fwd_pp_kernel<D, true, true, VARLEN><<<grid, 512, 0, st>>>(p);
+        else attn_fwd_pp_kernel<D, true, false, VARLEN><<<grid, 512, 0, st>>>(p);
+      } else {
+        if (drop) attn_fwd_pp_kernel<D, false, true, VARLEN><<<grid, 512, 0, st>>>(p);
+        else attn_fwd_pp_kernel<D, false, false, VARLEN><<<grid, 512, 0, st>>>(p);
+      }
+    } else if (p.causal) {
       if (drop) attn_fwd_bf16_kernel<D, true, true, VARLEN><<<grid, kThreads, 0, st>>>(p);
       else attn_fwd_bf16_kernel<D, true, false, VARLEN><<<grid, kThreads, 0, st>>>(p);
     } else {

@@ -283,7 +283,10 @@ def test_empty_batch_or_sequence(b, s):
 def test_forward_split_grid_and_unsplit_agree_with_the_oracle():
     """A small causal grid at d = 128 can split its longest query tiles over
     two workgroups (with a workspace) or not (without one): both match the
-    oracle, and the merged LSE equals the unsplit one to fp32 rounding."""
+    oracle, and the merged LSE equals the unsplit one to the rounding of the
+    row sums, which add the bf16-rounded probabilities (each within 2^-9 of
+    its value; the two launches round against different running maxima, so
+    their log-sums can differ by up to 2^-8)."""
     device = need_gpu()
     a = gen.AttnShape(b=1, s=384, hq=4, hkv=2, d=128, causal=True, p_drop=0.1, seed=21)
     announce("forward split vs unsplit")
@@ -300,7 +303,7 @@ def test_forward_split_grid_and_unsplit_agree_with_the_oracle():
     o_ref, lse_ref = oat.attn_fwd(x["q"], x["k"], x["v"], **kw)
     assert_close("o unsplit", host(o1), o_ref, TOL_BF16)
     assert_close("o split", host(o2), o_ref, TOL_BF16)
-    np.testing.assert_allclose(host(l2), host(l1), rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(host(l2), host(l1), rtol=0, atol=2.0**-8)
 
 
 PADDED = [
