@@ -535,6 +535,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
     for (int c = 0; c < kDC; ++c)
       qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
   }
+  // consumed here, so the compiler waits for these loads now and does not
+  // guard their later uses with waits that would also drain the tile loads
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) asm volatile("" ::"v"(qreg[c]));
 
   f32x16 oacc[kDB];
 #pragma unroll
@@ -552,36 +556,50 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
   const int key_lim = CAUSAL ? min(sl, qi + 1) : sl;
   auto tile_of = [&](int j) { return kt_lo + 2 * j + grp; };
 
-  // ---- staging of the group's tiles (chunk x = gtid + 256 it of a 64 x D tile)
-  uint4 kpre[kLoads], vpre[kLoads];
-  uint32_t koff[kLoads], voff[kLoads];
+  // ---- staging: buffer -> LDS loads.  One instruction fills 1 KB of LDS
+  // (lane l the bytes 16l .. 16l+15) from per-lane global offsets chosen so
+  // that the block lands in the padded layouts -- K rows in slot order, V
+  // rows in order -- without passing through registers; padding bytes are
+  // loaded from past the buffer's end, which reads zero.  The 4 waves of a
+  // group share a tile's blocks (wave w: blocks w, w+4, ...).
+  constexpr int kKBytes = kBN * kKS * 2, kVBytes = kBN * kVS * 2;
+  constexpr int kKBlocks = kKBytes / 1024, kVBlocks = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  constexpr int kKPer = (kKBlocks + 3) / 4, kVPer = (kVBlocks + 3) / 4;   // blocks of wave 0
+  // the fewest a wave issues per tile: the wait at the end of a VALU phase
+  // leaves that many of the wave's most recent loads in flight
+  constexpr int kRecent = kKBlocks / 4 + kVBlocks / 4;
+  uint32_t kdo[kKPer], vdo[kVPer];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) {
-    const int x = gtid + 256 * it;
-    koff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sk_s + 8 * (x % (D / 8))) * 2);
-    voff[it] = (uint32_t)(((int64_t)(x / (D / 8)) * p.sv_s + 8 * (x % (D / 8))) * 2);
+  for (int i = 0; i < kKPer; ++i) {
+    const int pos = 1024 * (wq + 4 * i) + 16 * lane;
+    const int row = pos / (2 * kKS), cb = pos % (2 * kKS);
+    const int key = (row & ~31) | perm32(row & 31);
+    kdo[i] = (row < kBN && cb < 2 * D) ? (uint32_t)((int64_t)key * p.sk_s * 2 + cb) : 0xFFFFFFF0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const int pos = 1024 * (wq + 4 * i) + 16 * lane;
+    const int row = pos / (2 * kVS), cb = pos % (2 * kVS);
+    vdo[i] = (row < kBN && cb < 2 * D) ? (uint32_t)((int64_t)row * p.sv_s * 2 + cb) : 0xFFFFFFF0u;
   }
   auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
     const int rows = kt < nkt ? min(kBN, max(0, sl - kt * kBN)) : 0;
     return (uint32_t)((int64_t)rows * stride * 2);
   };
-  auto load_kv = [&](int kt) {
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp + (int64_t)kt * kBN * p.sk_s, tile_bytes(kt, p.sk_s));
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + (int64_t)kt * kBN * p.sv_s, tile_bytes(kt, p.sv_s));
+  auto dma_k = [&](int kt, int buf) {
+    const sgpr4 rk = buffer_rsrc_sgpr(kp + (int64_t)kt * kBN * p.sk_s, tile_bytes(kt, p.sk_s));
+    const uintptr_t base = (uintptr_t)&sm.t.k[grp][buf][0];
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      kpre[it] = buffer_load16(rk, koff[it]);
-      vpre[it] = buffer_load16(rv, voff[it]);
-    }
+    for (int i = 0; i < kKPer; ++i)
+      if (wq + 4 * i < kKBlocks) buffer_load16_lds(rk, base + 1024 * (wq + 4 * i), kdo[i]);
   };
-  auto stash_kv = [&](int buf) {
+  auto dma_v = [&](int kt, int buf) {
+    const sgpr4 rv = buffer_rsrc_sgpr(vp + (int64_t)kt * kBN * p.sv_s, tile_bytes(kt, p.sv_s));
+    const uintptr_t base = (uintptr_t)&sm.t.v[grp][buf][0];
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      const int x = gtid + 256 * it;
-      const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.t.k[grp][buf][((r & ~31) | slot32(r & 31)) * kKS + 8 * c8]) = kpre[it];
-      *reinterpret_cast<uint4*>(&sm.t.v[grp][buf][r * kVS + 8 * c8]) = vpre[it];
-    }
+    for (int i = 0; i < kVPer; ++i)
+      if (wq + 4 * i < kVBlocks) buffer_load16_lds(rv, base + 1024 * (wq + 4 * i), vdo[i]);
   };
 
   const int krow = col * kKS + 8 * half;
@@ -627,10 +645,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
 
   // V phase of step j: stage the group's tile of step j+1, load step j+2;
   // softmax of step j's scores into pw (MASK: causal / tail masking needed)
+  // loads issued here: V of step j+1 (its buffer's tile was last read by
+  // PV(j-1) in M(j)) and K of step j+2 (its buffer's tile by QK(j) in M(j));
+  // the wait at the end of the phase completes those of V(j-1): K of step
+  // j+1 and V of step j, which M(j+1) reads
   auto phase_v = [&](int j, bool have, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
-    stash_kv((j + 1) & 1);
-    load_kv(tile_of(j + 2));
+    dma_v(tile_of(j + 1), (j + 1) & 1);
+    dma_k(tile_of(j + 2), j & 1);
     if (!have) return;
     const int key0 = tile_of(j) * kBN;
     uint32_t w[16];
@@ -682,30 +704,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
       }
   };
 
-  // ---- prologue: the group's step-0 tile resident, step 1 in flight
-  load_kv(tile_of(0));
-  stash_kv(0);
-  load_kv(tile_of(1));
+  // ---- prologue: K of step 0 resident; V of step 0 and K of step 1 in flight
+  dma_k(tile_of(0), 0);
+  dma_v(tile_of(0), 0);
+  dma_k(tile_of(1), 1);
+  wait_vmcnt<kRecent>();
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one phase behind
 
   // steps whose tile needs no masking for this wave: tile_of(j) < n_int
   const int j_int = max(0, min(nsteps, (min(n_int, nkt) - kt_lo - grp + 1) / 2));
   int j = 0;
+  // Inside the loop the barriers are bare (lds_barrier): a __syncthreads
+  // would also wait for every load in flight, the prefetched tiles included.
+  // Each wave instead completes its own LDS reads (lgkmcnt) and, at the end
+  // of a VALU phase, the loads the next MFMA phase reads (wait_vmcnt).
   for (; j < j_int; ++j) {
     phase_m(j, j > 0, true);
-    __syncthreads();
+    lds_barrier();
     phase_v(j, true, bool_c<false>{});
-    __syncthreads();
+    wait_vmcnt<kRecent>();
+    lds_barrier();
   }
   for (; j < nsteps; ++j) {
     const bool have = tile_of(j) < nkt;
     phase_m(j, j > 0, have);
-    __syncthreads();
+    lds_barrier();
     phase_v(j, have, bool_c<true>{});
-    __syncthreads();
+    wait_vmcnt<kRecent>();
+    lds_barrier();
   }
   phase_m(nsteps, nsteps > 0 && tile_of(nsteps - 1) < nkt, false);
+  wait_vmcnt<0>();                 // no load may land in LDS once it is reused below
   __syncthreads();
   if (grp == 0) __syncthreads();   // balances group 1's extra barrier
 

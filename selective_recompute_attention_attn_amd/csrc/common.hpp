@@ -106,6 +106,48 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0));
 }
 
+// Buffer -> LDS load of 16 bytes per lane (gfx950): lane l's bytes land at
+// LDS address lds + 16 l, with lds wave-uniform (it goes to M0); voffset is
+// the lane's byte offset into the buffer, past its end reading zero.  The
+// load counts on vmcnt like any buffer load; wait on it (wait_vmcnt) and then
+// a barrier before other waves read the bytes.
+//
+// Written as one asm statement (set M0, issue the load) with no outputs and a
+// memory clobber: the compiler then neither reorders memory accesses across
+// it nor treats it as a pending LDS store, which would make it wait for every
+// such load before the next LDS read (and drain all prefetching).  The caller
+// waits with wait_vmcnt; loads the compiler does not see can only make its
+// own vmcnt waits stricter, never insufficient.
+typedef uint32_t sgpr4 __attribute__((ext_vector_type(4)));
+// Buffer resource as four scalar registers: base (48 bits), stride 0, the
+// byte count, gfx9 word 3 (as buffer_rsrc above).
+__device__ __forceinline__ sgpr4 buffer_rsrc_sgpr(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  sgpr4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu;
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void buffer_load16_lds(sgpr4 r, uintptr_t lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)lds);
+  // M0 is reserved to the compiler, which uses it in these kernels for
+  // nothing else (no LDS-DMA builtins, no indirect register indexing)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voffset), "s"(r) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that waits only for the wave's own LDS accesses
+// (lgkmcnt), not for its loads in flight; one asm statement with a memory
+// clobber, so the compiler moves no memory access across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // LDS transpose read (gfx950): within each 16-lane group, lane j receives
 // mem16[addr(4*i + j/4) + j%4] for i = 0..3, where addr(x) is the address
 // supplied by lane x of the group.  A lane (4*i + t) pointing at row r0+i,
