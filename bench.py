@@ -13,7 +13,9 @@ sub-results.  Prints ONE JSON line.
                     [--sub NAME,NAME | --sub none] [--no-cpu-baseline]
 
 ms_per_step   wall clock of the K timed steps of the headline workload
-              (synchronised on both sides)
+              (synchronised on both sides); before the W warm-up steps each
+              workload runs its own steps untimed for 0.25 s, so that the
+              GPU clocks have settled
 value         attention-core fwd+bwd algorithmic TFLOP/s of the headline
               workload over K back-to-back fwd+bwd passes on rotating buffer
               sets, timed by one pair of HIP events (timing-only, no system
@@ -48,6 +50,7 @@ N_SETS = 8                      # rotated input/output sets: a set's inputs have
                                 # 256 MB last-level cache before it is used again
 COPY_CALIBRATION_BYTES = 1 << 29  # 512 MiB read + 512 MiB written per calibration copy
 COPY_CALIBRATION_REPS = 3
+SETTLE_S = 0.25                 # seconds of untimed steps before each workload's warm-up steps
 HEADLINE = "llama3-70b-t8"
 SUBS = ("gpt22b-t8", "gpt175b-t8", "gpt530b-t8")
 LARGEST_LAYERNORM = "gpt22b-t8"  # 1024 x 6144 rows: the largest LayerNorm region of the workloads
@@ -339,8 +342,24 @@ class Bench:
         ops.trace_enable(False)
         return trace
 
+    def settle(self, seconds=SETTLE_S):
+        """Runs the workload's own steps, untimed, for a fraction of a second
+        before the warm-up steps.  The GPU's clocks take some 30-40 ms of
+        this work to reach their steady level (launches before that run up
+        to 25 % slower, also right after other heavy work), so the timed
+        steps, and a profiler's per-kernel mean over the whole run, see the
+        steady clocks."""
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(N_SETS):
+                self.step(i)
+                i += 1
+            self.torch.cuda.synchronize()
+        return i
+
     def measure(self, steps, warmup, trace=True):
         a, n = self.w.attn, self.w.norm
+        self.settle()
         for i in range(warmup):
             self.step(i)
         self.torch.cuda.synchronize()

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the library's kernels.
 
-Two summaries, written as short text files:
+Three summaries, written as short text files:
 
 * ``stats``   -- a ``--kernel-trace --stats`` run: per-kernel call count and
   mean / min / max duration, as a markdown table.
@@ -11,6 +11,8 @@ Two summaries, written as short text files:
   per-launch HBM bytes of every library kernel are written as JSON together
   with a hash of the kernel's sources, so that a later change of the kernel
   invalidates the figure.
+* ``counters`` -- several ``--pmc`` passes of SQ/GRBM counters: per-kernel
+  instruction counts and unit busy / wave wait shares, as a markdown table.
 
     python -m selective_recompute_attention_attn_amd.profiling stats \\
         --csv <dir>/run_kernel_stats.csv --workload gpt22b-t8 --command "..."
@@ -84,15 +86,22 @@ def _mangled(full: str):
     return name, args
 
 
+# kernels that the library's trace reports under another entry's name: the
+# two-group forward at d = 128 is the bf16 forward
+TRACE_ALIASES = {"attn_fwd_pp": "attn_fwd_bf16"}
+
+
 def short_name(full: str) -> str:
     """'void srat::(anonymous namespace)::attn_bwd_dq_kernel<96, true>(srat::AttnParams)'
-    (or its mangled form) -> 'attn_bwd_dq'; names of other kernels are returned unchanged."""
+    (or its mangled form) -> 'attn_bwd_dq', the name the library's own trace
+    uses; names of other kernels are returned unchanged."""
     mg = _mangled(full)
     if mg and mg[0].endswith("_kernel"):
-        return mg[0][:-len("_kernel")]
+        k = mg[0][:-len("_kernel")]
+        return TRACE_ALIASES.get(k, k)
     m = (re.search(r"srat::(?:\(anonymous namespace\)::)?([A-Za-z0-9_]+?)_kernel\b", full)
          or re.match(r"([A-Za-z0-9_]+?)_kernel\(", full))
-    return m.group(1) if m else full
+    return TRACE_ALIASES.get(m.group(1), m.group(1)) if m else full
 
 
 def pretty_name(full: str) -> str:
@@ -202,6 +211,58 @@ def cmd_traffic(a):
     print(f"wrote {out}")
 
 
+def counter_means(paths):
+    """{library trace name: {counter: mean over dispatches}} over several --pmc passes."""
+    out = collections.defaultdict(dict)
+    for path in paths:
+        with open(path) as f:
+            counters = {_col(r, "Counter_Name", "Counter-Name") for r in csv.DictReader(f)}
+        for c in sorted(counters):
+            for full, vals in counter_per_dispatch(path, c).items():
+                k = short_name(full)
+                if k in KERNEL_SOURCES:
+                    out[k][c] = sum(vals) / len(vals)
+    return out
+
+
+COUNTER_NOTE = (
+    "Normalisation: kernel cycles = `GRBM_GUI_ACTIVE` / 8 XCDs; MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / "
+    "1024 SIMDs; VALU busy = 4 x `SQ_ACTIVE_INST_VALU` / 1024 SIMDs (the SQ counts it in units of 4 cycles); "
+    "LDS busy = `SQ_LDS_IDX_ACTIVE` / 256 CUs; all over the kernel cycles. The wave-time shares divide "
+    "`SQ_ACTIVE_INST_ANY` (issuing), `SQ_WAIT_INST_ANY` (waiting on an instruction dependency) and "
+    "`SQ_WAIT_ANY` (waiting on a memory or LDS counter) by `SQ_WAVE_CYCLES`.")
+
+
+def cmd_counters(a):
+    m = counter_means(a.csv)
+    lines = [f"# Issue counters: {a.workload}", "",
+             f"rocprofv3 counters, {len(a.csv)} passes (per dispatch, mean over the dispatches of each kernel). "
+             "Commands, from the repository root (TMPDIR=/tmp):", "", "```", *a.command, "```", "",
+             COUNTER_NOTE, "",
+             "| kernel | VALU insts | MFMA insts | LDS insts | kernel cycles | MFMA busy | VALU busy | LDS busy "
+             "| LDS bank conflicts / LDS busy | wave issuing | wave waiting on dependency | wave waiting on memory/LDS |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    nan = float("nan")
+    for k in KERNEL_SOURCES:
+        if k not in m:
+            continue
+        g = lambda c: m[k].get(c, nan)
+        cyc = g("GRBM_GUI_ACTIVE") / 8
+        wc = g("SQ_WAVE_CYCLES")
+        lds = g("SQ_LDS_IDX_ACTIVE")
+        lines.append(
+            f"| {k} | {g('SQ_INSTS_VALU'):.0f} | {g('SQ_INSTS_MFMA'):.0f} | {g('SQ_INSTS_LDS'):.0f} | {cyc:.0f} "
+            f"| {g('SQ_VALU_MFMA_BUSY_CYCLES') / 1024 / cyc:.0%} | {4 * g('SQ_ACTIVE_INST_VALU') / 1024 / cyc:.0%} "
+            f"| {lds / 256 / cyc:.0%} | {g('SQ_LDS_BANK_CONFLICT') / lds if lds else 0:.0%} "
+            f"| {g('SQ_ACTIVE_INST_ANY') / wc:.0%} | {g('SQ_WAIT_INST_ANY') / wc:.0%} | {g('SQ_WAIT_ANY') / wc:.0%} |")
+    if a.note:
+        lines += ["", a.note]
+    out = os.path.join(ROOT, "profiles", f"counters_{a.workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -217,8 +278,13 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True, action="append", help="one counter_collection.csv per pass")
+    c.add_argument("--command", required=True, action="append", help="the command of each pass")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--note", default="")
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
