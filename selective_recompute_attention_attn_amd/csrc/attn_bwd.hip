@@ -14,7 +14,9 @@
 //   dQ = dS K * scale,        dK = dS^T Q * scale
 //
 // Kernels on one stream, no atomics (results are deterministic):
-//   dq  : one workgroup per 128 queries, the forward's shape.  Its prologue
+//   dq  : one workgroup per 128 queries, the forward's shape (at d = 128 two
+//         groups of 4 waves over the same queries, alternating key tiles,
+//         as the forward at that head dim).  Its prologue
 //         forms D = rowsum(dO * O) for its queries (stored for dkdv); then it
 //         loops over 64-key tiles, recomputes S^T and dP^T, forms dS^T in
 //         registers and accumulates dQ^T += K^T dS^T (K^T through LDS
@@ -739,6 +741,327 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   }
 }
 
+// ============================================================== dQ, two key groups (d = 128)
+// At d = 128 the one-group dQ kernel needs ~400 registers per wave, so it
+// runs one wave per SIMD and nothing hides its latencies.  This variant runs
+// 8 waves in two groups of 4 over the same 128 queries; group g takes the
+// key tiles kt_lo + 2j + g, so each wave fits 256 registers and two waves
+// share a SIMD.  Group 1 runs one barrier phase behind group 0: while one
+// wave of a SIMD issues its MFMAs (phase M: dQ^T += K^T dS^T of its previous
+// tile, then S^T and dP^T of its current tile), the other forms dS on the
+// VALU (phase V).  At the end group 1 hands its dQ^T to group 0 through LDS.
+// K/V tiles go from the buffer to LDS without passing through registers
+// (buffer_load ... lds), K one step ahead (it is read again, transposed, in
+// the step after its own) and V two steps ahead.
+template <int D>
+struct alignas(16) DqPPSmem {
+  static constexpr int kKS = TileStride<D>::kValue;   // K: rows (S^T) and transposed (dQ^T)
+  static constexpr int kVS = RowStride<D>::kValue;    // V: rows only
+  union {
+    struct {
+      bf16 k[2][2][kQN * kKS];   // [group][buffer], rows in slot order
+      bf16 v[2][2][kQN * kVS];
+    } t;
+    float x[4][(D / 32) * 16][64];   // group 1's dQ^T accumulators
+  };
+};
+
+template <int D>
+constexpr bool kDqPingPong = D == 128;
+
+template <int D, bool CAUSAL, bool DROP, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
+  using SM = DqPPSmem<D>;
+  constexpr int kKS = SM::kKS;
+  constexpr int kVS = SM::kVS;
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  __shared__ SM sm;
+
+  const int nqt = (p.s + kQM - 1) / kQM;
+  const int nbh = p.b * p.hq;
+  const int bh = blockIdx.x % nbh;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int nsq = kSplitBwd<D, CAUSAL> ? p.split_qt : 0;
+  int qt, part = -1;
+  if (nsq > 0) {
+    split_order(rank, nqt, nsq, qt, part);
+  } else {
+    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+  }
+  const int hh_q = bh % p.hq, bb = bh / p.hq;
+  const int g = hh_q / (p.hq / p.hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
+  const int grp = wv >> 2, wq = wv & 3;                       // key group, query block
+  const int half = lane >> 5, col = lane & 31;
+  const int q0 = qt * kQM;
+  const int qw = q0 + 32 * wq;
+  const int qi = qw + col;
+  const bool qvalid = qi < p.s;
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;
+  const bool qlive = VARLEN ? qi < sl : qvalid;
+
+  const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
+  const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
+  const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
+  const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
+  const int64_t row0 = ((int64_t)bb * p.hq + hh_q) * p.s;
+
+  // Q^T and dO^T B operands (as the one-group kernel), D = rowsum(dO * O)
+  bf16x8 qreg[kDC], doreg[kDC];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) qreg[c] = doreg[c] = bf16x8{};
+  if (qlive) {
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      qreg[c] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.sq_s + 16 * c + 8 * half);
+      doreg[c] = *reinterpret_cast<const bf16x8*>(dop + (int64_t)qi * p.so_s + 16 * c + 8 * half);
+    }
+  }
+  const float lse2 = qlive ? p.lse[row0 + qi] * kLog2e : 0.f;
+  float dlt = 0.f;
+  if (qlive) {
+    const bf16* orow = static_cast<const bf16*>(p.o) + bb * p.so_b + hh_q * p.so_h + (int64_t)qi * p.so_s;
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 16 * c + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf(bf2f(ov[e]), bf2f(doreg[c][e]), dlt);
+    }
+  }
+  dlt = halves_sum(dlt);
+  if (grp == 0 && qvalid && half == 0 && part <= 0) p.delta[row0 + qi] = dlt;
+  // consumed here, so the compiler waits for these loads now and does not
+  // guard their later uses with waits that would also drain the tile loads
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) asm volatile("" ::"v"(qreg[c]), "v"(doreg[c]));
+  asm volatile("" ::"v"(lse2));
+  // the tile loads are counted on vmcnt after everything issued so far
+  wait_vmcnt<0>();
+
+  f32x16 qacc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) qacc[db] = f32x16{};
+
+  const int nkt_all = (sl + kQN - 1) / kQN;
+  const int nkt_q = CAUSAL ? min(nkt_all, (q0 + kQM + kQN - 1) / kQN) : nkt_all;
+  const int kt_mid = (nkt_q + 1) / 2;
+  const int kt_lo = part == 1 ? kt_mid : 0;
+  const int nkt = part == 0 ? kt_mid : nkt_q;                      // key tiles [kt_lo, nkt)
+  const int nsteps = (nkt - kt_lo + 1) / 2;                        // steps of both groups
+  const int n_int = (VARLEN && qw + 31 >= sl) ? 0 : CAUSAL ? min(sl / kQN, (qw + 1) / kQN) : sl / kQN;
+  const int key_lim = VARLEN ? (qlive ? (CAUSAL ? min(sl, qi + 1) : sl) : 0) : (CAUSAL ? min(p.s, qi + 1) : p.s);
+  auto tile_of = [&](int j) { return kt_lo + 2 * j + grp; };
+
+  // ---- staging: buffer -> LDS loads, 1 KB of LDS per instruction (lane l
+  // the bytes 16l .. 16l+15), per-lane global offsets that land K and V in
+  // slot order in the padded layouts; padding reads from past the buffer's
+  // end, which gives zero.  The 4 waves of a group share a tile's blocks.
+  constexpr int kKBytes = kQN * kKS * 2, kVBytes = kQN * kVS * 2;
+  constexpr int kKBlocks = kKBytes / 1024, kVBlocks = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  constexpr int kKPer = (kKBlocks + 3) / 4, kVPer = (kVBlocks + 3) / 4;
+  // the fewest V blocks a wave issues per tile: the wait at the end of a V
+  // phase leaves that many of the wave's most recent loads (V, two steps
+  // ahead) in flight and completes everything before them
+  constexpr int kRecent = kVBlocks / 4;
+  uint32_t kdo[kKPer], vdo[kVPer];
+#pragma unroll
+  for (int i = 0; i < kKPer; ++i) {
+    const int pos = 1024 * (wq + 4 * i) + 16 * lane;
+    const int row = pos / (2 * kKS), cb = pos % (2 * kKS);
+    const int key = (row & ~31) | perm32(row & 31);
+    kdo[i] = (row < kQN && cb < 2 * D) ? (uint32_t)((int64_t)key * p.sk_s * 2 + cb) : 0xFFFFFFF0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const int pos = 1024 * (wq + 4 * i) + 16 * lane;
+    const int row = pos / (2 * kVS), cb = pos % (2 * kVS);
+    const int key = (row & ~31) | perm32(row & 31);
+    vdo[i] = (row < kQN && cb < 2 * D) ? (uint32_t)((int64_t)key * p.sv_s * 2 + cb) : 0xFFFFFFF0u;
+  }
+  auto tile_bytes = [&](int kt, int64_t stride) -> uint32_t {
+    const int rows = kt < nkt ? min(kQN, max(0, sl - kt * kQN)) : 0;
+    return (uint32_t)((int64_t)rows * stride * 2);
+  };
+  auto dma_k = [&](int kt, int buf) {
+    const sgpr4 rk = buffer_rsrc_sgpr(kp + (int64_t)kt * kQN * p.sk_s, tile_bytes(kt, p.sk_s));
+    const uintptr_t base = (uintptr_t)&sm.t.k[grp][buf][0];
+#pragma unroll
+    for (int i = 0; i < kKPer; ++i)
+      if (wq + 4 * i < kKBlocks) buffer_load16_lds(rk, base + 1024 * (wq + 4 * i), kdo[i]);
+  };
+  auto dma_v = [&](int kt, int buf) {
+    const sgpr4 rv = buffer_rsrc_sgpr(vp + (int64_t)kt * kQN * p.sv_s, tile_bytes(kt, p.sv_s));
+    const uintptr_t base = (uintptr_t)&sm.t.v[grp][buf][0];
+#pragma unroll
+    for (int i = 0; i < kVPer; ++i)
+      if (wq + 4 * i < kVBlocks) buffer_load16_lds(rv, base + 1024 * (wq + 4 * i), vdo[i]);
+  };
+
+  const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+  const PhiloxRow prow = philox_row((uint32_t)qi, hg, (uint32_t)bb, p.k0, p.k1);
+  const uint32_t thr_hi = p.thresh << 16;
+  const float c2 = p.scale_log2;
+  const int kro = col * kKS + 8 * half;
+  const int vro = col * kVS + 8 * half;
+  const int lgp = lane >> 4, lg = lane & 15;
+  const int ktr = (4 * (lgp >> 1) + (lg >> 2)) * kKS + 16 * (lgp & 1) + 4 * (lg & 3);
+  auto kt_operand = [&](const bf16* kb_, int c, int db) -> bf16x8 {
+    const int r0 = (32 * (c >> 1) + 16 * (c & 1)) * kKS + ktr;
+    const s16x4 lo = lds_read_tr16(&kb_[r0 + 32 * db]);
+    const s16x4 hi = lds_read_tr16(&kb_[r0 + 8 * kKS + 32 * db]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 sacc[2], pacc[2];   // S^T, dP^T of the current tile
+  uint32_t dsw[16];          // dS^T of the previous tile, packed bf16 pairs
+
+  // M phase of step j: dQ^T += K^T dS^T of step j-1 (if it had a tile), then
+  // S^T = K Q^T and dP^T = V dO^T of step j
+  auto phase_m = [&](int j, bool dq, bool sp) {
+    if (dq) {
+      const bf16* kb_ = sm.t.k[grp][(j - 1) & 1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 dsop =
+            __builtin_bit_cast(bf16x8, make_uint4(dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]));
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) qacc[db] = mfma32(kt_operand(kb_, c, db), dsop, qacc[db]);
+      }
+    }
+    if (sp) {
+      const bf16* kb_ = sm.t.k[grp][j & 1];
+      const bf16* vb = sm.t.v[grp][j & 1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = pacc[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&kb_[32 * kb * kKS + kro + 16 * c]), qreg[c], sacc[kb]);
+          pacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&vb[32 * kb * kVS + vro + 16 * c]), doreg[c], pacc[kb]);
+        }
+    }
+  };
+
+  // V phase of step j: load K of step j+1 (its buffer's tile, step j-1, was
+  // last read by M(j)) and V of step j+2 (its buffer's tile, step j, too);
+  // form dS^T of step j into dsw (MASK: causal / tail masking needed)
+  auto phase_v = [&](int j, bool have, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    dma_k(tile_of(j + 1), (j + 1) & 1);
+    dma_v(tile_of(j + 2), j & 1);
+    if (!have) return;
+    const int key0 = tile_of(j) * kQN;
+    uint32_t w[16];
+    if (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {
+          const Philox4 rnd = philox4x32_10_row((uint32_t)((key0 + 32 * kb + 16 * half + 8 * gh) >> 3), prow);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) w[8 * kb + 4 * gh + jj] = rnd.w[jj];
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float pv[2], dp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + e], c2, -lse2));
+          if (MASK) pv[e] = key0 + 32 * kb + 16 * half + r + e >= key_lim ? 0.f : pv[e];
+          dp[e] = pacc[kb][r + e];
+        }
+        if (DROP) {
+          const uint32_t ww = w[8 * kb + (r >> 1)];
+          dp[0] = (ww & 0xFFFFu) >= p.thresh ? dp[0] : 0.f;
+          dp[1] = ww >= thr_hi ? dp[1] : 0.f;
+        }
+        dsw[8 * kb + (r >> 1)] =
+            pack_bf16x2(pv[0] * fmaf(dp[0], p.inv_keep, -dlt), pv[1] * fmaf(dp[1], p.inv_keep, -dlt));
+      }
+  };
+
+  // ---- prologue: K and V of step 0 resident, V of step 1 in flight
+  dma_k(tile_of(0), 0);
+  dma_v(tile_of(0), 0);
+  dma_v(tile_of(1), 1);
+  wait_vmcnt<kRecent>();
+  __syncthreads();
+  if (grp == 1) __syncthreads();   // group 1 runs one phase behind
+
+  // steps whose tile needs no masking for this wave: tile_of(j) < n_int
+  const int j_int = max(0, min(nsteps, (min(n_int, nkt) - kt_lo - grp + 1) / 2));
+  int j = 0;
+  // bare barriers in the loop (see lds_barrier): each wave completes its own
+  // LDS reads and, at the end of a V phase, the loads the next M phase reads
+  for (; j < j_int; ++j) {
+    phase_m(j, j > 0, true);
+    lds_barrier();
+    phase_v(j, true, bool_c<false>{});
+    wait_vmcnt<kRecent>();
+    lds_barrier();
+  }
+  for (; j < nsteps; ++j) {
+    const bool have = tile_of(j) < nkt;
+    phase_m(j, j > 0, have);
+    lds_barrier();
+    phase_v(j, have, bool_c<true>{});
+    wait_vmcnt<kRecent>();
+    lds_barrier();
+  }
+  phase_m(nsteps, nsteps > 0 && tile_of(nsteps - 1) < nkt, false);
+  wait_vmcnt<0>();                 // no load may land in LDS once it is reused below
+  __syncthreads();
+  if (grp == 0) __syncthreads();   // balances group 1's extra barrier
+
+  // ---- group 1's dQ^T into group 0's (both over the same queries)
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.x[wq][db * 16 + r][lane] = qacc[db][r];
+  }
+  __syncthreads();
+  if (grp == 1) return;
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) qacc[db][r] += sm.x[wq][db * 16 + r][lane];
+
+  // ---- store (as the one-group kernel)
+  if (part >= 0) {
+    if (qvalid) {
+      float* dst = p.dq_part + (((int64_t)part * p.b * p.hq * p.s) + row0 + qi) * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * half) =
+              make_float4(qacc[db][4 * a], qacc[db][4 * a + 1], qacc[db][4 * a + 2], qacc[db][4 * a + 3]);
+    }
+    return;
+  }
+  if (qvalid) {
+    bf16* dq = static_cast<bf16*>(p.dq) + bb * p.sq_b + (int64_t)qi * p.sq_s + hh_q * p.sq_h;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 wo;
+        wo.x = pack_bf16x2(qacc[db][4 * a + 0] * p.scale, qacc[db][4 * a + 1] * p.scale);
+        wo.y = pack_bf16x2(qacc[db][4 * a + 2] * p.scale, qacc[db][4 * a + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dq + 32 * db + 8 * a + 4 * half) = wo;
+      }
+    }
+  }
+}
+
 // ============================================================== partial sums
 // dK, dV of a kv-head = the sum of its fp32 partials: over the q-heads that
 // share it (grouped-query attention) and over the two parts of a split key
@@ -819,7 +1142,10 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
   {
     TraceScope ts("attn_bwd_dq", st);
     const unsigned nqt = (unsigned)((p.s + kQM - 1) / kQM);
-    attn_bwd_dq_kernel<D, CAUSAL, DROP, VARLEN><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
+    if constexpr (kDqPingPong<D>)
+      attn_bwd_dq_pp_kernel<D, CAUSAL, DROP, VARLEN><<<(nqt + p.split_qt) * nbh, 512, 0, st>>>(p);
+    else
+      attn_bwd_dq_kernel<D, CAUSAL, DROP, VARLEN><<<(nqt + p.split_qt) * nbh, 256, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
