@@ -23,7 +23,9 @@
 //         transpose reads).  Re-doing QK^T and dO V^T here costs MFMA work
 //         (not counted in the algorithmic FLOPs) but removes every atomic
 //         from the backward.
-//   dkdv: one workgroup per (128-key block, q-head, batch).  Waves split the
+//   dkdv: one workgroup per (128-key block, q-head, batch) (at d = 128 with
+//         the chain below split between producer and consumer waves, see
+//         attn_bwd_dkdv_pc_kernel).  Waves split the
 //         block's keys into four 32-key groups (and, for head dims <= 64, each
 //         64-query tile into two 32-query halves, one wave per pair).  A wave
 //         computes S^T = K Q^T and dP^T = V dO^T with its K, V rows as
@@ -447,6 +449,288 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
       const float dvv = dv_acc[db][r] * p.inv_keep;
       const float dkv = dk_acc[db][r] * p.scale;
       const int dcol = 32 * (d0 + db) + col;
+      if (PART || part >= 0) {   // slot 1 holds the second parts of split blocks
+        const int64_t o = ((int64_t)max(part, 0) * p.b * p.s * p.hq + ((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
+        p.dv_acc[o] = dvv;
+        p.dk_acc[o] = dkv;
+      } else {
+        static_cast<bf16*>(p.dv)[bb * p.sv_b + (int64_t)key * p.sv_s + g * p.sv_h + dcol] = (bf16)dvv;
+        static_cast<bf16*>(p.dk)[bb * p.sk_b + (int64_t)key * p.sk_s + g * p.sk_h + dcol] = (bf16)dkv;
+      }
+    }
+  }
+}
+
+// ============================================================== dK, dV: producer and consumer waves (d = 128)
+// At d = 128 one wave of the kernel above holds K and V rows (64 registers),
+// both accumulators (128) and a tile's scores, so it runs alone on its SIMD
+// and each 32-query tile is a serial chain: S^T, dP^T MFMAs -> softmax
+// recompute and dS on the VALU -> LDS round trip -> dV, dK MFMAs.  Here the
+// two halves of that chain run in different waves.  Waves 0-3 (producers)
+// hold the K and V rows of their 32 keys, compute S^T and dP^T, and write
+// P*M and dS to LDS; waves 4-7 (consumers, one per SIMD beside a producer)
+// hold the dK and dV accumulators of the same keys and, one tile behind,
+// read P*M and dS back transposed for dV += (P*M)^T dO and dK += dS^T Q.
+// The roles run separate loops with one barrier per step, so each fits 256
+// registers and a producer's VALU work overlaps its SIMD neighbour's MFMAs.
+// Q, dO and the tile's LSE and D reach LDS through buffer -> LDS loads in a
+// four-slot ring, two tiles ahead of the producers.
+template <int D>
+struct alignas(16) DkdvPCSmem {
+  static constexpr int kS = TileStride<D>::kValue;            // Q / dO row stride (bf16)
+  static constexpr int kQBlocks = (32 * kS * 2 + 1023) / 1024;  // 1 KB blocks of a Q (dO) tile
+  static constexpr int kBlocks = (2 * kQBlocks + 2 + 7) / 8 * 8;   // per slot: Q, dO, LSE, D, slack
+  unsigned char ring[4][kBlocks * 1024];
+  bf16 pm[2][4][kWaveTile];   // [step parity][key group]
+  bf16 ds[2][4][kWaveTile];
+};
+
+template <int D>
+constexpr bool kDkdvPC = D == 128;
+
+template <int D, bool CAUSAL, bool DROP, bool PART, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) {
+  using SM = DkdvPCSmem<D>;
+  constexpr int kS = SM::kS;
+  constexpr int kQBlocks = SM::kQBlocks, kBlocks = SM::kBlocks;
+  constexpr int kPer = kBlocks / 8;   // ring blocks each wave loads per tile
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kRows = 32;
+  __shared__ SM sm;
+
+  const int nbh = p.b * p.hq;
+  const int nkb = (p.s + kBNk - 1) / kBNk;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int nsk = kSplitBwd<D, CAUSAL> ? p.split_kb : 0;
+  int kblk, part = -1;
+  if (nsk > 0) {
+    int t;
+    split_order(rank, nkb, nsk, t, part);
+    kblk = nkb - 1 - t;
+  } else {
+    kblk = rank;   // ascending: the blocks with the most queries first
+  }
+  const int bh = (int)(blockIdx.x % nbh);
+  const int hh_q = bh % p.hq, bb = bh / p.hq;
+  const int g = hh_q / (p.hq / p.hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
+  const int role = wv >> 2, kg = wv & 3;                      // producer / consumer, key group
+  const int half = lane >> 5, col = lane & 31;
+  const int k0 = kblk * kBNk;
+  const int kw0 = k0 + 32 * kg;
+  const int sl = VARLEN ? attn_len(p, bb) : p.s;
+
+  const bf16* qp = static_cast<const bf16*>(p.q) + bb * p.sq_b + hh_q * p.sq_h;
+  const bf16* dop = static_cast<const bf16*>(p.dout) + bb * p.so_b + hh_q * p.so_h;
+  const bf16* kp = static_cast<const bf16*>(p.k) + bb * p.sk_b + g * p.sk_h;
+  const bf16* vp = static_cast<const bf16*>(p.v) + bb * p.sv_b + g * p.sv_h;
+  const int64_t row0 = ((int64_t)bb * p.hq + hh_q) * p.s;
+
+  const int nqt_all = (sl + kRows - 1) / kRows;
+  const int qt_first = CAUSAL ? k0 / kRows : 0;
+  const int qt_mid = qt_first + (nqt_all - qt_first + 1) / 2;
+  const int qt0 = part == 1 ? qt_mid : qt_first;
+  const int nqt = part == 0 ? qt_mid : nqt_all;
+  // tiles of this workgroup (none for a key block past the valid length)
+  const int n = (VARLEN && k0 >= sl) ? 0 : nqt - qt0;
+
+  // ---- ring staging: slot = [Q tile | dO tile | LSE of its 32 queries |
+  // D of them | slack], 1 KB per load instruction (lane l: bytes 16l ..),
+  // wave w loading blocks w, w + 8, ...; Q and dO rows land in the padded
+  // row layout, padding and everything past the tile read as zero
+  uint32_t doff[kPer];
+  int dsel[kPer];   // 0 Q, 1 dO, 2 LSE, 3 D, 4 slack
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int blk = wv + 8 * i;
+    uint32_t off = 0xFFFFFFF0u;
+    int sel = 4;
+    if (blk < 2 * kQBlocks) {
+      sel = blk < kQBlocks ? 0 : 1;
+      const int pos = 1024 * (blk - sel * kQBlocks) + 16 * lane;
+      const int row = pos / (2 * kS), cb = pos % (2 * kS);
+      const int64_t rs = sel == 0 ? p.sq_s : p.so_s;
+      if (row < kRows && cb < 2 * D) off = (uint32_t)((int64_t)row * rs * 2 + cb);
+    } else if (blk < 2 * kQBlocks + 2) {
+      sel = 2 + (blk - 2 * kQBlocks);
+      if (lane < kRows / 4) off = 16u * lane;
+    }
+    doff[i] = off;
+    dsel[i] = sel;
+  }
+  auto dma = [&](int qt, int slot) {
+    const int rows = qt < nqt ? min(kRows, max(0, sl - qt * kRows)) : 0;
+    const sgpr4 rq = buffer_rsrc_sgpr(qp + (int64_t)qt * kRows * p.sq_s, (uint32_t)((int64_t)rows * p.sq_s * 2));
+    const sgpr4 ro = buffer_rsrc_sgpr(dop + (int64_t)qt * kRows * p.so_s, (uint32_t)((int64_t)rows * p.so_s * 2));
+    const sgpr4 rl = buffer_rsrc_sgpr(p.lse + row0 + (int64_t)qt * kRows, (uint32_t)rows * 4u);
+    const sgpr4 rd = buffer_rsrc_sgpr(p.delta + row0 + (int64_t)qt * kRows, (uint32_t)rows * 4u);
+    const uintptr_t base = (uintptr_t)&sm.ring[slot][0];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int sel = dsel[i];
+      const sgpr4 r = sel == 0 ? rq : sel == 1 ? ro : sel == 2 ? rl : rd;
+      buffer_load16_lds(r, base + 1024 * (wv + 8 * i), doff[i]);
+    }
+  };
+  auto q_of = [&](int slot) { return reinterpret_cast<const bf16*>(&sm.ring[slot][0]); };
+  auto do_of = [&](int slot) { return reinterpret_cast<const bf16*>(&sm.ring[slot][kQBlocks * 1024]); };
+  auto stat_of = [&](int slot, int which) {
+    return reinterpret_cast<const float*>(&sm.ring[slot][(2 * kQBlocks + which) * 1024]);
+  };
+  const int w_row = col * kWaveRow + 16 * half;   // this lane's 16 keys in the wave tiles
+
+  if (role == 0) {
+    // ================= producer: S^T, dP^T, P*M and dS of each tile
+    bf16x8 kreg[kDC], vreg[kDC];
+    {
+      const int key = kw0 + perm32(col);
+      const bool ok = key < sl;
+      const int64_t ko = (int64_t)(ok ? key : 0) * p.sk_s + 8 * half;
+      const int64_t vo = (int64_t)(ok ? key : 0) * p.sv_s + 8 * half;
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kp + ko + 16 * c);
+        const uint4 b = *reinterpret_cast<const uint4*>(vp + vo + 16 * c);
+        kreg[c] = __builtin_bit_cast(bf16x8, ok ? a : make_uint4(0, 0, 0, 0));
+        vreg[c] = __builtin_bit_cast(bf16x8, ok ? b : make_uint4(0, 0, 0, 0));
+      }
+    }
+    // consumed here, so the compiler waits for these loads now and does not
+    // guard their later uses with waits that would also drain the ring loads
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) asm volatile("" ::"v"(kreg[c]), "v"(vreg[c]));
+    wait_vmcnt<0>();
+
+    const uint32_t hg = (uint32_t)(p.head_offset + hh_q);
+    const uint32_t thr_hi = p.thresh << 16;
+    const float c2 = p.scale_log2;
+    PhiloxCol pcol[2];
+    if (DROP) {
+#pragma unroll
+      for (int gh = 0; gh < 2; ++gh)
+        pcol[gh] = philox_col((uint32_t)((kw0 + 16 * half + 8 * gh) >> 3), hg, (uint32_t)bb, p.k0, p.k1);
+    }
+    const int q_row = col * kS + 8 * half;   // this lane's Q / dO row (B operands)
+    const int key_l = kw0 + 16 * half;
+    // tiles this wave computes without masking: [qa, qb)
+    int qa = qt0, qb = qt0;
+    if (kw0 + 32 <= sl) {
+      qa = CAUSAL ? max(qt0, (kw0 + 31 + kRows - 1) / kRows) : qt0;
+      qb = (sl - 32) < 0 ? qa : min(nqt, max(qa, (sl - 32) / kRows + 1));
+    }
+
+    auto produce = [&](int qt, int slot, int pbuf, auto mask_c) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const int qi = qt * kRows + col;
+      const bf16* qb_ = q_of(slot);
+      const bf16* ob_ = do_of(slot);
+      const float lse2 = stat_of(slot, 0)[col] * kLog2e;
+      const float dlt = stat_of(slot, 1)[col];
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&qb_[q_row + 16 * c]), sacc);
+        pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&ob_[q_row + 16 * c]), pacc);
+      }
+      Philox4 rnd[2];
+      if (DROP) {
+        rnd[0] = philox4x32_10_col((uint32_t)qi, pcol[0]);
+        rnd[1] = philox4x32_10_col((uint32_t)qi, pcol[1]);
+      }
+      const int kl = qi < sl ? (CAUSAL ? min(sl, qi + 1) : sl) : 0;
+      uint32_t pmw[8], dsw[8];
+#pragma unroll
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float pv[2], dp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * r2 + e;
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, -lse2));
+          if (MASK) pv[e] = key_l + r >= kl ? 0.f : pv[e];
+          dp[e] = pacc[r];
+        }
+        uint32_t pk = pack_bf16x2(pv[0], pv[1]);
+        if (DROP) {
+          const uint32_t w = rnd[r2 >> 2].w[r2 & 3];
+          const bool keep0 = (w & 0xFFFFu) >= p.thresh, keep1 = w >= thr_hi;
+          pk = and_or(pk, keep0 ? 0xFFFFu : 0u, keep1 ? 0xFFFF0000u : 0u);
+          dp[0] = keep0 ? dp[0] : 0.f;
+          dp[1] = keep1 ? dp[1] : 0.f;
+        }
+        pmw[r2] = pk;
+        dsw[r2] = pack_bf16x2(pv[0] * fmaf(dp[0], p.inv_keep, -dlt), pv[1] * fmaf(dp[1], p.inv_keep, -dlt));
+      }
+      bf16* pmt = sm.pm[pbuf][kg];
+      bf16* dst = sm.ds[pbuf][kg];
+      *reinterpret_cast<uint4*>(&pmt[w_row]) = make_uint4(pmw[0], pmw[1], pmw[2], pmw[3]);
+      *reinterpret_cast<uint4*>(&pmt[w_row + 8]) = make_uint4(pmw[4], pmw[5], pmw[6], pmw[7]);
+      *reinterpret_cast<uint4*>(&dst[w_row]) = make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]);
+      *reinterpret_cast<uint4*>(&dst[w_row + 8]) = make_uint4(dsw[4], dsw[5], dsw[6], dsw[7]);
+    };
+
+    dma(qt0, 0);
+    dma(qt0 + 1, 1);
+    // step k: tile k of the producers (the consumers take tile k - 1); the
+    // barrier bare (see lds_barrier): each wave has completed its own loads
+    // of tile k, and the consumers their reads of the slot the next load reuses
+    for (int k = 0; k <= n; ++k) {
+      wait_vmcnt<kPer>();
+      lds_barrier();
+      dma(qt0 + k + 2, (k + 2) & 3);
+      if (k < n) {
+        const int qt = qt0 + k;
+        if (qt >= qa && qt < qb) produce(qt, k & 3, k & 1, bool_c<false>{});
+        else produce(qt, k & 3, k & 1, bool_c<true>{});
+      }
+    }
+    wait_vmcnt<0>();
+    return;
+  }
+
+  // ================= consumer: dV += (P*M)^T dO, dK += dS^T Q, one tile behind
+  f32x16 dv_acc[kDB], dk_acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) dv_acc[db] = dk_acc[db] = f32x16{};
+  const int tr_w = 16 * ((lane >> 4) & 1) + (8 * (lane >> 5) + ((lane & 15) >> 2)) * kWaveRow + 4 * (lane & 3);
+  const int tr_s = tr_off32(kS, lane);
+  auto consume = [&](int slot, int pbuf) {
+    const bf16* qb_ = q_of(slot);
+    const bf16* ob_ = do_of(slot);
+    const bf16* pmt = sm.pm[pbuf][kg];
+    const bf16* dst = sm.ds[pbuf][kg];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 apm = tr_pair(&pmt[16 * st * kWaveRow + tr_w], kWaveRow);
+      const bf16x8 ads = tr_pair(&dst[16 * st * kWaveRow + tr_w], kWaveRow);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        dv_acc[db] = mfma32(apm, tr_pair(&ob_[16 * st * kS + tr_s + 32 * db], kS), dv_acc[db]);
+        dk_acc[db] = mfma32(ads, tr_pair(&qb_[16 * st * kS + tr_s + 32 * db], kS), dk_acc[db]);
+      }
+    }
+  };
+  dma(qt0, 0);
+  dma(qt0 + 1, 1);
+  for (int k = 0; k <= n; ++k) {
+    wait_vmcnt<kPer>();
+    lds_barrier();
+    dma(qt0 + k + 2, (k + 2) & 3);
+    if (k >= 1) consume((k - 1) & 3, (k - 1) & 1);
+  }
+  wait_vmcnt<0>();
+
+  // store: lane holds d = 32db + col, keys kw0 + 8*(r/4) + 4*half + r%4
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key >= p.s) continue;
+      const float dvv = dv_acc[db][r] * p.inv_keep;
+      const float dkv = dk_acc[db][r] * p.scale;
+      const int dcol = 32 * db + col;
       if (PART || part >= 0) {   // slot 1 holds the second parts of split blocks
         const int64_t o = ((int64_t)max(part, 0) * p.b * p.s * p.hq + ((int64_t)bb * p.s + key) * p.hq + hh_q) * D + dcol;
         p.dv_acc[o] = dvv;
@@ -1154,8 +1438,13 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
     const unsigned nkb = (unsigned)((p.s + kBNk - 1) / kBNk);
     const dim3 grid((nkb + p.split_kb) * nbh * DkdvCfg<D>::kDParts);
     const int threads = 256 * DkdvCfg<D>::kQH;
-    if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, threads, 0, st>>>(p);
-    else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, threads, 0, st>>>(p);
+    if constexpr (kDkdvPC<D>) {
+      if (part) attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, 512, 0, st>>>(p);
+      else attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, 512, 0, st>>>(p);
+    } else {
+      if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, threads, 0, st>>>(p);
+      else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, threads, 0, st>>>(p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
