@@ -23,7 +23,7 @@
 //         transpose reads).  Re-doing QK^T and dO V^T here costs MFMA work
 //         (not counted in the algorithmic FLOPs) but removes every atomic
 //         from the backward.
-//   dkdv: one workgroup per (128-key block, q-head, batch) (at d = 128 with
+//   dkdv: one workgroup per (128-key block, q-head, batch) (at d = 128, 160 with
 //         the chain below split between producer and consumer waves, see
 //         attn_bwd_dkdv_pc_kernel).  Waves split the
 //         block's keys into four 32-key groups (and, for head dims <= 64, each
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
   }
 }
 
-// ============================================================== dK, dV: producer and consumer waves (d = 128)
+// ============================================================== dK, dV: producer and consumer waves (d = 128, 160)
 // At d = 128 one wave of the kernel above holds K and V rows (64 registers),
 // both accumulators (128) and a tile's scores, so it runs alone on its SIMD
 // and each 32-query tile is a serial chain: S^T, dP^T MFMAs -> softmax
@@ -485,8 +485,10 @@ struct alignas(16) DkdvPCSmem {
   bf16 ds[2][4][kWaveTile];
 };
 
+// (at d = 96 the kernel above already runs two workgroups per CU, and the
+// split measured slower there: gpt22b-t8 shape 92 -> 98 us)
 template <int D>
-constexpr bool kDkdvPC = D == 128;
+constexpr bool kDkdvPC = D == 128 || D == 160;
 
 template <int D, bool CAUSAL, bool DROP, bool PART, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) {
