@@ -87,8 +87,9 @@ def _mangled(full: str):
 
 
 # kernels that the library's trace reports under another entry's name: the
-# two-group forward at d = 128 is the bf16 forward
-TRACE_ALIASES = {"attn_fwd_pp": "attn_fwd_bf16"}
+# two-group forward and dQ kernels and the producer/consumer dK/dV kernel
+# (d = 128, 160) stand in for the one-group kernels there
+TRACE_ALIASES = {"attn_fwd_pp": "attn_fwd_bf16", "attn_bwd_dq_pp": "attn_bwd_dq", "attn_bwd_dkdv_pc": "attn_bwd_dkdv"}
 
 
 def short_name(full: str) -> str:

@@ -10,9 +10,13 @@ def test_demangled_names():
                                 "(srat::AttnParams, int, int, int)") == "attn_bwd_sums"
 
 
-def test_two_group_forward_reports_as_the_bf16_forward():
+def test_two_group_kernels_report_under_the_library_trace_names():
     assert profiling.short_name("void srat::(anonymous namespace)::attn_fwd_pp_kernel<128, true, false, false>"
                                 "(srat::AttnParams)") == "attn_fwd_bf16"
+    assert profiling.short_name("void srat::(anonymous namespace)::attn_bwd_dq_pp_kernel<128, true, false, false>"
+                                "(srat::AttnParams)") == "attn_bwd_dq"
+    assert profiling.short_name("_ZN4srat12_GLOBAL__N_123attn_bwd_dkdv_pc_kernelILi128ELb1ELb0ELb1ELb0EEEvNS_10AttnParamsE"
+                                ) == "attn_bwd_dkdv"
 
 
 def test_mangled_names_with_bf16_arguments():
