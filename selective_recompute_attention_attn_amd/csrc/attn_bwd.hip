@@ -1052,6 +1052,8 @@ struct alignas(16) DqPPSmem {
   };
 };
 
+// (at d = 96 two one-group workgroups already share a CU, and the two-group
+// form measured slower there: gpt22b-t8 shape 67 -> 88 us)
 template <int D>
 constexpr bool kDqPingPong = D == 128;
 
@@ -1148,10 +1150,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
   constexpr int kKBlocks = kKBytes / 1024, kVBlocks = kVBytes / 1024;
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
   constexpr int kKPer = (kKBlocks + 3) / 4, kVPer = (kVBlocks + 3) / 4;
-  // the fewest V blocks a wave issues per tile: the wait at the end of a V
-  // phase leaves that many of the wave's most recent loads (V, two steps
-  // ahead) in flight and completes everything before them
-  constexpr int kRecent = kVBlocks / 4;
+  // the V blocks wave w issues per tile: the wait at the end of a V phase
+  // leaves exactly those (its most recent loads: V, two steps ahead) in
+  // flight and completes everything before them
+  auto wait_recent = [&] {
+    wait_vmcnt_by_wave<blocks_of_wave(kVBlocks, 0), blocks_of_wave(kVBlocks, 1), blocks_of_wave(kVBlocks, 2),
+                       blocks_of_wave(kVBlocks, 3)>(wq);
+  };
   uint32_t kdo[kKPer], vdo[kVPer];
 #pragma unroll
   for (int i = 0; i < kKPer; ++i) {
@@ -1277,7 +1282,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
   dma_k(tile_of(0), 0);
   dma_v(tile_of(0), 0);
   dma_v(tile_of(1), 1);
-  wait_vmcnt<kRecent>();
+  wait_recent();
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one phase behind
 
@@ -1290,7 +1295,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
     phase_m(j, j > 0, true);
     lds_barrier();
     phase_v(j, true, bool_c<false>{});
-    wait_vmcnt<kRecent>();
+    wait_recent();
     lds_barrier();
   }
   for (; j < nsteps; ++j) {
@@ -1298,7 +1303,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
     phase_m(j, j > 0, have);
     lds_barrier();
     phase_v(j, have, bool_c<true>{});
-    wait_vmcnt<kRecent>();
+    wait_recent();
     lds_barrier();
   }
   phase_m(nsteps, nsteps > 0 && tile_of(nsteps - 1) < nkt, false);

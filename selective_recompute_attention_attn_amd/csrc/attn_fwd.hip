@@ -476,7 +476,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
   constexpr int kVS = SM::kVS;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kLoads = D / 32;     // 16-byte loads per thread per 64 x D tile (a group's 256 threads)
   __shared__ SM sm;
 
   const int nqt = (p.s + kBM - 1) / kBM;
@@ -496,7 +495,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile bounds scalar
   const int grp = wv >> 2, wq = wv & 3;                       // key group, query block
-  const int gtid = tid & 255;                                 // thread within the group
   const int half = lane >> 5, col = lane & 31;
   const int q0 = qt * kBM;
   const int qw = q0 + 32 * wq;
@@ -566,9 +564,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
   constexpr int kKBlocks = kKBytes / 1024, kVBlocks = kVBytes / 1024;
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
   constexpr int kKPer = (kKBlocks + 3) / 4, kVPer = (kVBlocks + 3) / 4;   // blocks of wave 0
-  // the fewest a wave issues per tile: the wait at the end of a VALU phase
-  // leaves that many of the wave's most recent loads in flight
-  constexpr int kRecent = kKBlocks / 4 + kVBlocks / 4;
+  // the loads wave w issues per phase: the wait at the end of a VALU phase
+  // leaves exactly those (its most recent) in flight and completes the rest
+  auto wait_recent = [&] {
+    wait_vmcnt_by_wave<blocks_of_wave(kKBlocks, 0) + blocks_of_wave(kVBlocks, 0),
+                       blocks_of_wave(kKBlocks, 1) + blocks_of_wave(kVBlocks, 1),
+                       blocks_of_wave(kKBlocks, 2) + blocks_of_wave(kVBlocks, 2),
+                       blocks_of_wave(kKBlocks, 3) + blocks_of_wave(kVBlocks, 3)>(wq);
+  };
   uint32_t kdo[kKPer], vdo[kVPer];
 #pragma unroll
   for (int i = 0; i < kKPer; ++i) {
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
   dma_k(tile_of(0), 0);
   dma_v(tile_of(0), 0);
   dma_k(tile_of(1), 1);
-  wait_vmcnt<kRecent>();
+  wait_recent();
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one phase behind
 
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
     phase_m(j, j > 0, true);
     lds_barrier();
     phase_v(j, true, bool_c<false>{});
-    wait_vmcnt<kRecent>();
+    wait_recent();
     lds_barrier();
   }
   for (; j < nsteps; ++j) {
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnParams p) {
     phase_m(j, j > 0, have);
     lds_barrier();
     phase_v(j, have, bool_c<true>{});
-    wait_vmcnt<kRecent>();
+    wait_recent();
     lds_barrier();
   }
   phase_m(nsteps, nsteps > 0 && tile_of(nsteps - 1) < nkt, false);

@@ -141,6 +141,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Blocks b < nblocks with b = w (mod 4): the buffer -> LDS loads wave w of a
+// 4-wave group issues for one tile when the group shares its blocks out.
+__host__ __device__ constexpr int blocks_of_wave(int nblocks, int w) { return (nblocks - w + 3) / 4; }
+// wait_vmcnt<N> with N = the count of the wave's most recent loads that may
+// stay in flight, which differs between the waves of a group (wave-uniform
+// branch on w = 0..3)
+template <int N0, int N1, int N2, int N3>
+__device__ __forceinline__ void wait_vmcnt_by_wave(int w) {
+  if (w == 0) wait_vmcnt<N0>();
+  else if (w == 1) wait_vmcnt<N1>();
+  else if (w == 2) wait_vmcnt<N2>();
+  else wait_vmcnt<N3>();
+}
+
 // Workgroup barrier that waits only for the wave's own LDS accesses
 // (lgkmcnt), not for its loads in flight; one asm statement with a memory
 // clobber, so the compiler moves no memory access across it.
