@@ -760,7 +760,11 @@ struct alignas(16) DqSmem {
   bf16 v[2][kQN * kVS];
 };
 
+// Causal q-tile order: paired (two workgroups per CU: block i and block
+// i + grid/2 carry equal work) or longest first (one per CU), as in the forward.
+template <bool PAIRED>
 __device__ __forceinline__ int causal_tile(int rank, int nqt) {
+  if (!PAIRED) return nqt - 1 - rank;
   const int h = (nqt + 1) / 2;
   return rank < h ? nqt - 1 - rank : rank - h;
 }
@@ -789,7 +793,7 @@ __global__ __launch_bounds__(256, DqOcc<D>::kWavesPerEU) void attn_bwd_dq_kernel
   if (nsq > 0) {
     split_order(rank, nqt, nsq, qt, part);
   } else {
-    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+    qt = CAUSAL ? causal_tile<DqOcc<D>::kWavesPerEU == 2>(rank, nqt) : rank;
   }
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
@@ -1075,7 +1079,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(AttnParams p) {
   if (nsq > 0) {
     split_order(rank, nqt, nsq, qt, part);
   } else {
-    qt = CAUSAL ? causal_tile(rank, nqt) : rank;
+    qt = CAUSAL ? causal_tile<false>(rank, nqt) : rank;
   }
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
