@@ -18,10 +18,16 @@ def _rel(x, ref):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("causal,p", [(True, 0.1), (False, 0.0)])
-def test_layer_matches_oracle(causal, p):
+@pytest.mark.parametrize("s,b,h,hq,d,ffn,causal,p", [
+    (96, 2, 128, 2, 64, 256, True, 0.1),
+    (96, 2, 128, 2, 64, 256, False, 0.0),
+    # d = 128: the two-group forward and dQ kernels and the producer/consumer
+    # dK/dV kernel, three 128-query tiles (the longest split), 8 heads
+    (384, 1, 1024, 8, 128, 2048, True, 0.1),
+    (384, 1, 1024, 8, 128, 2048, True, 0.0),
+])
+def test_layer_matches_oracle(s, b, h, hq, d, ffn, causal, p):
     device = need_gpu()
-    s, b, h, hq, d, ffn = 96, 2, 128, 2, 64, 256
     announce(f"layer s={s} b={b} h={h} hq={hq} d={d} ffn={ffn} causal={causal} p={p}")
     w = gl.random_weights(h, hq, d, ffn, device=device, seed=4)
     layer = gl.Layer(w, hq=hq, d=d, causal=causal, p_attn=p, p_hidden=p, seed=9)
