@@ -79,6 +79,8 @@ SMALL = [
     (1, 384, 4, 2, 128, True, 0.1),
     (1, 300, 2, 2, 128, False, 0.3),
     (1, 261, 2, 2, 160, True, 0.1),
+    (2, 150, 4, 2, 160, False, 0.1),   # producer/consumer dK/dV: grouped, non-causal, dropout
+    (1, 190, 4, 1, 128, False, 0.2),   # two-group forward / dQ, producer/consumer dK/dV: 4:1, non-causal
     (2, 128, 8, 1, 128, True, 0.0),
     (1, 333, 2, 2, 192, True, 0.1),
     (2, 200, 4, 2, 192, False, 0.0),
