@@ -474,7 +474,11 @@ __global__ __launch_bounds__(256 * DkdvCfg<D>::kQH, DkdvCfg<D>::kBlocksPerCU) vo
 // The roles run separate loops with one barrier per step, so each fits 256
 // registers and a producer's VALU work overlaps its SIMD neighbour's MFMAs.
 // Q, dO and the tile's LSE and D reach LDS through buffer -> LDS loads in a
-// four-slot ring, two tiles ahead of the producers.
+// four-slot ring, two tiles ahead of the producers.  The producers issue all
+// of them, behind their MFMAs: the issue of 24 KB of loads per step stalls
+// the issuing waves for hundreds of cycles (address processing), which right
+// after the barrier delayed the consumers (the critical path) and the
+// producers' MFMAs.
 template <int D>
 struct alignas(16) DkdvPCSmem {
   static constexpr int kS = TileStride<D>::kValue;            // Q / dO row stride (bf16)
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
   using SM = DkdvPCSmem<D>;
   constexpr int kS = SM::kS;
   constexpr int kQBlocks = SM::kQBlocks, kBlocks = SM::kBlocks;
-  constexpr int kPer = kBlocks / 8;   // ring blocks each wave loads per tile
+  constexpr int kPer = kBlocks / 4;   // ring blocks each producer wave loads per tile
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kRows = 32;
@@ -540,13 +544,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
 
   // ---- ring staging: slot = [Q tile | dO tile | LSE of its 32 queries |
   // D of them | slack], 1 KB per load instruction (lane l: bytes 16l ..),
-  // wave w loading blocks w, w + 8, ...; Q and dO rows land in the padded
-  // row layout, padding and everything past the tile read as zero
+  // producer wave kg loading blocks kg, kg + 4, ...; Q and dO rows land in
+  // the padded row layout, padding and everything past the tile read as zero
   uint32_t doff[kPer];
   int dsel[kPer];   // 0 Q, 1 dO, 2 LSE, 3 D, 4 slack
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int blk = wv + 8 * i;
+    const int blk = kg + 4 * i;
     uint32_t off = 0xFFFFFFF0u;
     int sel = 4;
     if (blk < 2 * kQBlocks) {
@@ -563,6 +567,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
     dsel[i] = sel;
   }
   auto dma = [&](int qt, int slot) {
+    if (role != 0) return;   // the producers load the ring; the consumers are the critical path
     const int rows = qt < nqt ? min(kRows, max(0, sl - qt * kRows)) : 0;
     const sgpr4 rq = buffer_rsrc_sgpr(qp + (int64_t)qt * kRows * p.sq_s, (uint32_t)((int64_t)rows * p.sq_s * 2));
     const sgpr4 ro = buffer_rsrc_sgpr(dop + (int64_t)qt * kRows * p.so_s, (uint32_t)((int64_t)rows * p.so_s * 2));
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
     for (int i = 0; i < kPer; ++i) {
       const int sel = dsel[i];
       const sgpr4 r = sel == 0 ? rq : sel == 1 ? ro : sel == 2 ? rl : rd;
-      buffer_load16_lds(r, base + 1024 * (wv + 8 * i), doff[i]);
+      buffer_load16_lds(r, base + 1024 * (kg + 4 * i), doff[i]);
     }
   };
   auto q_of = [&](int slot) { return reinterpret_cast<const bf16*>(&sm.ring[slot][0]); };
@@ -623,7 +628,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
       qb = (sl - 32) < 0 ? qa : min(nqt, max(qa, (sl - 32) / kRows + 1));
     }
 
-    auto produce = [&](int qt, int slot, int pbuf, auto mask_c) {
+    auto produce = [&](int qt, int slot, int pbuf, int ld_qt, int ld_slot, auto mask_c) {
       constexpr bool MASK = decltype(mask_c)::value;
       const int qi = qt * kRows + col;
       const bf16* qb_ = q_of(slot);
@@ -636,6 +641,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
         sacc = mfma32(kreg[c], *reinterpret_cast<const bf16x8*>(&qb_[q_row + 16 * c]), sacc);
         pacc = mfma32(vreg[c], *reinterpret_cast<const bf16x8*>(&ob_[q_row + 16 * c]), pacc);
       }
+      dma(ld_qt, ld_slot);   // issued behind the MFMAs
       Philox4 rnd[2];
       if (DROP) {
         rnd[0] = philox4x32_10_col((uint32_t)qi, pcol[0]);
@@ -680,11 +686,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
     for (int k = 0; k <= n; ++k) {
       wait_vmcnt<kPer>();
       lds_barrier();
-      dma(qt0 + k + 2, (k + 2) & 3);
       if (k < n) {
         const int qt = qt0 + k;
-        if (qt >= qa && qt < qb) produce(qt, k & 3, k & 1, bool_c<false>{});
-        else produce(qt, k & 3, k & 1, bool_c<true>{});
+        if (qt >= qa && qt < qb) produce(qt, k & 3, k & 1, qt0 + k + 2, (k + 2) & 3, bool_c<false>{});
+        else produce(qt, k & 3, k & 1, qt0 + k + 2, (k + 2) & 3, bool_c<true>{});
+      } else {
+        dma(qt0 + k + 2, (k + 2) & 3);
       }
     }
     wait_vmcnt<0>();
@@ -713,12 +720,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
       }
     }
   };
-  dma(qt0, 0);
-  dma(qt0 + 1, 1);
   for (int k = 0; k <= n; ++k) {
-    wait_vmcnt<kPer>();
     lds_barrier();
-    dma(qt0 + k + 2, (k + 2) & 3);
     if (k >= 1) consume((k - 1) & 3, (k - 1) & 1);
   }
   wait_vmcnt<0>();
