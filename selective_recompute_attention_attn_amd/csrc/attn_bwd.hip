@@ -494,8 +494,9 @@ struct alignas(16) DkdvPCSmem {
 template <int D>
 constexpr bool kDkdvPC = D == 128 || D == 160;
 
+// One 128-key block (kblk; part 0 / 1: one half of its query range, -1: all).
 template <int D, bool CAUSAL, bool DROP, bool PART, bool VARLEN>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) {
+__device__ __forceinline__ void dkdv_pc_tile(const AttnParams& p, DkdvPCSmem<D>& sm, int bh, int kblk, int part) {
   using SM = DkdvPCSmem<D>;
   constexpr int kS = SM::kS;
   constexpr int kQBlocks = SM::kQBlocks, kBlocks = SM::kBlocks;
@@ -503,21 +504,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kRows = 32;
-  __shared__ SM sm;
 
-  const int nbh = p.b * p.hq;
-  const int nkb = (p.s + kBNk - 1) / kBNk;
-  const int rank = (int)(blockIdx.x / nbh);
-  const int nsk = kSplitBwd<D, CAUSAL> ? p.split_kb : 0;
-  int kblk, part = -1;
-  if (nsk > 0) {
-    int t;
-    split_order(rank, nkb, nsk, t, part);
-    kblk = nkb - 1 - t;
-  } else {
-    kblk = rank;   // ascending: the blocks with the most queries first
-  }
-  const int bh = (int)(blockIdx.x % nbh);
   const int hh_q = bh % p.hq, bb = bh / p.hq;
   const int g = hh_q / (p.hq / p.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -745,6 +732,38 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) 
         static_cast<bf16*>(p.dk)[bb * p.sk_b + (int64_t)key * p.sk_s + g * p.sk_h + dcol] = (bf16)dkv;
       }
     }
+  }
+}
+
+// Block order: PAIRED (causal, unsplit) gives workgroup t the key blocks t
+// and n-1-t; a split grid runs in decreasing modelled work (split_order);
+// otherwise ascending (the blocks with the most queries first).
+template <int D, bool CAUSAL, bool DROP, bool PART, bool VARLEN, bool PAIRED>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pc_kernel(AttnParams p) {
+  __shared__ DkdvPCSmem<D> sm;
+  const int nbh = p.b * p.hq;
+  const int nkb = (p.s + kBNk - 1) / kBNk;
+  const int rank = (int)(blockIdx.x / nbh);
+  const int bh = (int)(blockIdx.x % nbh);
+  if constexpr (PAIRED) {
+    const int b1 = nkb - 1 - rank;
+    const int nblk = rank < b1 ? 2 : 1;
+#pragma nounroll
+    for (int i = 0; i < nblk; ++i) {
+      if (i > 0) __syncthreads();   // the first block's consumers have read the ring
+      dkdv_pc_tile<D, CAUSAL, DROP, PART, VARLEN>(p, sm, bh, i == 0 ? rank : b1, -1);
+    }
+  } else {
+    const int nsk = kSplitBwd<D, CAUSAL> ? p.split_kb : 0;
+    int kblk, part = -1;
+    if (nsk > 0) {
+      int t;
+      split_order(rank, nkb, nsk, t, part);
+      kblk = nkb - 1 - t;
+    } else {
+      kblk = rank;
+    }
+    dkdv_pc_tile<D, CAUSAL, DROP, PART, VARLEN>(p, sm, bh, kblk, part);
   }
 }
 
@@ -1453,8 +1472,14 @@ hipError_t bwd_main(const AttnParams& p, hipStream_t st) {
     const dim3 grid((nkb + p.split_kb) * nbh * DkdvCfg<D>::kDParts);
     const int threads = 256 * DkdvCfg<D>::kQH;
     if constexpr (kDkdvPC<D>) {
-      if (part) attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, 512, 0, st>>>(p);
-      else attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, 512, 0, st>>>(p);
+      if (CAUSAL && attn_pair_tiles(p, (int)nkb, p.split_kb)) {
+        const dim3 gp((nkb + 1) / 2 * nbh);
+        if (part) attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, true, VARLEN, CAUSAL><<<gp, 512, 0, st>>>(p);
+        else attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, false, VARLEN, CAUSAL><<<gp, 512, 0, st>>>(p);
+      } else {
+        if (part) attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, true, VARLEN, false><<<grid, 512, 0, st>>>(p);
+        else attn_bwd_dkdv_pc_kernel<D, CAUSAL, DROP, false, VARLEN, false><<<grid, 512, 0, st>>>(p);
+      }
     } else {
       if (part) attn_bwd_dkdv_kernel<D, CAUSAL, DROP, true, VARLEN><<<grid, threads, 0, st>>>(p);
       else attn_bwd_dkdv_kernel<D, CAUSAL, DROP, false, VARLEN><<<grid, threads, 0, st>>>(p);

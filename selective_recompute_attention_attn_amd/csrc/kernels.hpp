@@ -89,6 +89,15 @@ struct AttnParams {
   int32_t split_kb;    // backward: 128-key blocks whose queries are split over two dK/dV workgroups
 };
 
+// Compute units of the MI355X (gfx950).  An unsplit causal dK/dV grid whose
+// workgroups, taking two key blocks each (t and n-1-t: the same work for
+// every workgroup), still cover them all runs paired: one dispatch per CU
+// and no longest-first tail.
+constexpr int kNumCUs = 256;
+inline bool attn_pair_tiles(const AttnParams& p, int ntiles, int nsplit) {
+  return p.causal && nsplit == 0 && (int64_t)p.b * p.hq * (ntiles / 2) >= kNumCUs;
+}
+
 // Work split for grids too small to fill the chip (causal, one workgroup per
 // CU): the longest query tiles / key blocks are halved so that no workgroup
 // carries much more than half the longest one's work; the halves write fp32

@@ -204,6 +204,24 @@ def test_head_offset_split_invariance():
             np.testing.assert_array_equal(part[n], full[n][:, :, lo:lo + 2])
 
 
+def test_paired_grid_equals_unpaired():
+    """At d = 128 a causal dK/dV grid with enough (batch, head) pairs runs two
+    key blocks per workgroup (blocks t and n-1-t); each block's arithmetic is
+    unchanged, so the heads it shares with a smaller, unpaired grid come out
+    bit for bit the same (forward and dQ included)."""
+    device = need_gpu()
+    a = gen.AttnShape(b=1, s=2048, hq=32, hkv=32, d=128, causal=True, p_drop=0.1, seed=11)
+    announce("paired grid (32 heads) against unpaired (24 heads)")
+    x = gen.attn_inputs(a)
+    full = run_gpu(a, x, device)                  # 32 x 8 pairs: paired
+    sub = {n: x[n][:, :, :24] for n in x}
+    part = run_gpu(a.with_(hq=24, hkv=24), sub, device)   # 24 x 8 < 256: not paired, not split
+    np.testing.assert_array_equal(part["o"], full["o"][:, :, :24])
+    np.testing.assert_array_equal(part["lse"], full["lse"][:, :24])
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(part[n], full[n][:, :, :24])
+
+
 def test_no_s_by_s_allocation():
     device = need_gpu()
     a = gen.AttnShape(b=1, s=4096, hq=8, hkv=1, d=128, causal=True, p_drop=0.0)
@@ -317,6 +335,8 @@ PADDED = [
     (2, 300, 2, 2, 192, True, 0.1, [300, 111]),
     (2, 260, 2, 1, 256, True, 0.1, [260, 99]),
     (4, 2048, 8, 8, 96, True, 0.1, [2048, 1500, 700, 31]),
+    # 32 (batch, head) pairs of 16 key blocks: the d = 128 dK/dV grid runs paired
+    (2, 2048, 16, 16, 128, True, 0.1, [2048, 1337]),
 ]
 
 
@@ -335,7 +355,7 @@ def test_padded_batch(b, s, hq, hkv, d, causal, p, lens):
     o, lse = ops.attn_core_fwd(q, k, v, seqlens=sl, **kw)
     dq, dk, dv = ops.attn_core_bwd(q, k, v, o, lse, do, seqlens=sl, **kw)
     torch.cuda.synchronize()
-    heads = None if s <= 512 else [(0, 0), (1, 3), (2, 5), (3, 7)]
+    heads = None if s <= 512 else [(0, 0), (1, 3), (2, 5), (3, 7)][:b]
     o_r, lse_r = oat.attn_fwd(x["q"], x["k"], x["v"], heads=heads, seqlens=lens, **kw)
     dq_r, dk_r, dv_r = oat.attn_bwd(x["q"], x["k"], x["v"], lse_r, x["do"], heads=heads, seqlens=lens, **kw)
     tq, tk = grad_term_scales(x, o_r, lse_r, heads=heads, seqlens=lens, **kw)
