@@ -89,7 +89,21 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("b,s,hq,hkv,d,causal,p", SMALL)
+def _swept_shapes(n=20, seed=2026):
+    """Seeded draws over the supported space: every head dim, grouped-query
+    ratios, lengths from 1 to 320 (tails of every tile size), causal or not,
+    with and without dropout."""
+    r = np.random.RandomState(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(r.choice([1, 2, 3]))
+        hq = hkv * int(r.choice([1, 2, 4]))
+        out.append((int(r.randint(1, 3)), int(r.randint(1, 321)), hq, hkv, int(r.choice([32, 64, 96, 128, 160, 192, 256])),
+                    bool(r.randint(2)), float(r.choice([0.0, 0.1, 0.25]))))
+    return out
+
+
+@pytest.mark.parametrize("b,s,hq,hkv,d,causal,p", SMALL + _swept_shapes())
 def test_bf16_small_shapes(b, s, hq, hkv, d, causal, p):
     device = need_gpu()
     a = gen.AttnShape(b=b, s=s, hq=hq, hkv=hkv, d=d, causal=causal, p_drop=p, seed=1234, head_offset=3)
